@@ -1,0 +1,298 @@
+"""Checks that pin the oracle to something other than itself.
+
+Each check takes an ``oracle.Oracle`` and raises ``AssertionError`` on a mismatch. They are run against
+the real oracle (tests/test_oracle_*.py) and against copies of ``oracle.c`` with planted mistakes
+(tests/test_oracle_mutants.py), which must each fail at least one check.
+
+What pins what:
+* the pages' worked examples (slot flattening, block split) -- tests/test_golden_host.py;
+* closed forms of softmax attention (one key; zero query; constant values; equal keys; two keys
+  with a known score gap);
+* ``torch.nn.functional.scaled_dot_product_attention`` in float64 on K/V gathered by numpy
+  indexing from a pool laid out as ``[num_blocks, num_kv_heads, block_size, head_dim]``, with an
+  explicit bottom-right causal mask for chunked prefill;
+* invariants: permuting physical block ids, GQA versus MHA with repeated KV heads, decode versus the
+  last row of causal prefill, chunk-split invariance.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from workloads import F32, blocks_for_tokens
+
+
+def _rand_pool(rng, nb, hkv, bs, d):
+    kc = rng.standard_normal((nb, hkv, bs, d)).astype(np.float32)
+    vc = rng.standard_normal((nb, hkv, bs, d)).astype(np.float32)
+    return kc, vc
+
+
+def _tables(rng, lens, bs, nb, stride=None):
+    nbs = [blocks_for_tokens(n, bs) for n in lens]
+    perm = rng.permutation(nb).astype(np.int32)
+    stride = stride or max(max(nbs), 1)
+    bt = np.full((len(lens), stride), -1, np.int32)
+    off = 0
+    for i, k in enumerate(nbs):
+        bt[i, :k] = perm[off:off + k]
+        off += k
+    return bt
+
+
+def numpy_gather(kc, bt_row, n):
+    """Logical rows [0, n) of one table, by numpy indexing: [n, Hkv, D]."""
+    bs = kc.shape[2]
+    t = np.arange(n)
+    return kc[bt_row[t // bs], :, t % bs, :].astype(np.float64)   # advanced axes first: [n, Hkv, D]
+
+
+def sdpa64(q, k, v, scale, mask=None):
+    """Library attention in float64. q [Hq, Lq, D], k/v [Hq, Lk, D]."""
+    tq = torch.from_numpy(np.ascontiguousarray(q, np.float64))[None]
+    tk = torch.from_numpy(np.ascontiguousarray(k, np.float64))[None]
+    tv = torch.from_numpy(np.ascontiguousarray(v, np.float64))[None]
+    am = None if mask is None else torch.from_numpy(mask)[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=am, scale=scale)
+    return o[0].numpy()
+
+
+# ---- closed forms --------------------------------------------------------------------------------
+
+def check_single_key(orc):
+    """One cached token: the output is that token's value row, exactly."""
+    rng = np.random.default_rng(11)
+    kc, vc = _rand_pool(rng, 8, 2, 4, 8)
+    bt = np.array([[5, -1]], np.int32)
+    q = rng.standard_normal((1, 4, 8)).astype(np.float32)
+    out = orc.decode(F32, q, kc, vc, bt, np.array([1], np.int32), 0.3)
+    for h in range(4):
+        assert np.array_equal(out[0, h], vc[5, h // 2, 0].astype(np.float64))
+
+
+def check_zero_query(orc):
+    """q = 0: every score ties, the output is the mean of the value rows."""
+    rng = np.random.default_rng(12)
+    kc, vc = _rand_pool(rng, 16, 2, 4, 8)
+    lens = [7, 13]
+    bt = _tables(rng, lens, 4, 16)
+    q = np.zeros((2, 2, 8), np.float32)
+    out = orc.decode(F32, q, kc, vc, bt, np.array(lens, np.int32), 1.0)
+    for i, n in enumerate(lens):
+        v = numpy_gather(vc, bt[i], n)
+        for h in range(2):
+            np.testing.assert_allclose(out[i, h], v[:, h].mean(axis=0), rtol=0, atol=1e-12)
+
+
+def check_constant_values(orc):
+    """All value rows equal c: the output is c whatever the scores."""
+    rng = np.random.default_rng(13)
+    kc, vc = _rand_pool(rng, 16, 1, 4, 8)
+    c = rng.standard_normal(8).astype(np.float32)
+    vc[:] = c
+    bt = _tables(rng, [11], 4, 16)
+    q = (3 * rng.standard_normal((1, 2, 8))).astype(np.float32)
+    out = orc.decode(F32, q, kc, vc, bt, np.array([11], np.int32), 0.7)
+    np.testing.assert_allclose(out[0], np.broadcast_to(c, (2, 8)), rtol=0, atol=1e-12)
+
+
+def check_equal_keys(orc):
+    """All key rows equal: every score ties, the output is the mean of the value rows."""
+    rng = np.random.default_rng(14)
+    kc, vc = _rand_pool(rng, 16, 2, 4, 8)
+    kc[:] = rng.standard_normal(8).astype(np.float32)
+    bt = _tables(rng, [9], 4, 16)
+    q = rng.standard_normal((1, 4, 8)).astype(np.float32)
+    out = orc.decode(F32, q, kc, vc, bt, np.array([9], np.int32), 0.5)
+    v = numpy_gather(vc, bt[0], 9)
+    for h in range(4):
+        np.testing.assert_allclose(out[0, h], v[:, h // 2].mean(axis=0), rtol=0, atol=1e-12)
+
+
+def check_two_keys_known_gap(orc):
+    """Two keys whose scaled scores differ by g: weights are sigmoid(g) and 1 - sigmoid(g).
+    q = e0, k0 = a e0, k1 = b e0 -> s0 - s1 = scale (a - b)."""
+    d, scale, a, b = 8, 0.25, 3.0, -1.0
+    kc = np.zeros((2, 1, 2, d), np.float32)
+    vc = np.zeros((2, 1, 2, d), np.float32)
+    kc[1, 0, 0, 0], kc[1, 0, 1, 0] = a, b           # logical tokens 0, 1 live in physical block 1
+    vc[1, 0, 0, :] = 1.0
+    vc[1, 0, 1, :] = -2.0
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = 1.0
+    out = orc.decode(F32, q, kc, vc, np.array([[1]], np.int32), np.array([2], np.int32), scale)
+    w0 = 1.0 / (1.0 + math.exp(-scale * (a - b)))
+    np.testing.assert_allclose(out[0, 0], np.full(d, w0 * 1.0 + (1 - w0) * -2.0), rtol=0, atol=1e-12)
+
+
+# ---- library routine -----------------------------------------------------------------------------
+
+def check_decode_vs_sdpa(orc, hq=8, hkv=2, d=16, bs=4, lens=(1, 3, 4, 5, 9, 17), seed=21):
+    rng = np.random.default_rng(seed)
+    nb = sum(blocks_for_tokens(n, bs) for n in lens) + 3
+    kc, vc = _rand_pool(rng, nb, hkv, bs, d)
+    bt = _tables(rng, lens, bs, nb)
+    q = rng.standard_normal((len(lens), hq, d)).astype(np.float32)
+    scale = 1.0 / math.sqrt(d)
+    out = orc.decode(F32, q, kc, vc, bt, np.array(lens, np.int32), scale)
+    g = hq // hkv
+    for i, n in enumerate(lens):
+        k = numpy_gather(kc, bt[i], n).transpose(1, 0, 2).repeat(g, axis=0)
+        v = numpy_gather(vc, bt[i], n).transpose(1, 0, 2).repeat(g, axis=0)
+        ref = sdpa64(q[i][:, None, :].astype(np.float64), k, v, scale)[:, 0, :]
+        np.testing.assert_allclose(out[i], ref, rtol=1e-12, atol=1e-12)
+
+
+def _prefill_setup(rng, prefix, chunk, hq, hkv, d, bs, extra_blocks=2):
+    lk = [p + c for p, c in zip(prefix, chunk)]
+    nb = sum(blocks_for_tokens(n, bs) for n in lk) + extra_blocks
+    kc, vc = _rand_pool(rng, nb, hkv, bs, d)
+    bt = _tables(rng, lk, bs, nb)
+    cu_q = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    q = rng.standard_normal((int(cu_q[-1]), hq, d)).astype(np.float32)
+    return kc, vc, bt, cu_q, cu_k, q
+
+
+def check_prefill_vs_sdpa(orc, causal=True, seed=22):
+    prefix, chunk = [0, 3, 5, 8], [4, 1, 6, 3]
+    hq, hkv, d, bs = 4, 2, 8, 4
+    rng = np.random.default_rng(seed)
+    kc, vc, bt, cu_q, cu_k, q = _prefill_setup(rng, prefix, chunk, hq, hkv, d, bs)
+    scale = 0.4
+    out = orc.prefill(F32, q, kc, vc, bt, cu_q, cu_k, scale, causal=causal)
+    g = hq // hkv
+    for i, (p, c) in enumerate(zip(prefix, chunk)):
+        lk = p + c
+        k = numpy_gather(kc, bt[i], lk).transpose(1, 0, 2).repeat(g, axis=0)
+        v = numpy_gather(vc, bt[i], lk).transpose(1, 0, 2).repeat(g, axis=0)
+        qi = q[cu_q[i]:cu_q[i + 1]].transpose(1, 0, 2).astype(np.float64)
+        mask = None
+        if causal:
+            mask = np.arange(lk)[None, :] <= (p + np.arange(c))[:, None]     # bottom-right aligned
+        ref = sdpa64(qi, k, v, scale, mask).transpose(1, 0, 2)
+        np.testing.assert_allclose(out[cu_q[i]:cu_q[i + 1]], ref, rtol=1e-12, atol=1e-12)
+
+
+# ---- invariants ----------------------------------------------------------------------------------
+
+def check_block_permutation_invariance(orc, seed=31):
+    """Moving every physical block to a new id and rewriting the tables leaves outputs bit-identical."""
+    rng = np.random.default_rng(seed)
+    lens = [5, 12, 1, 16]
+    bs, nb = 4, 20
+    kc, vc = _rand_pool(rng, nb, 2, bs, 8)
+    bt = _tables(rng, lens, bs, nb)
+    q = rng.standard_normal((4, 4, 8)).astype(np.float32)
+    cl = np.array(lens, np.int32)
+    a = orc.decode(F32, q, kc, vc, bt, cl, 0.3)
+    perm = rng.permutation(nb)
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[perm] = kc
+    vc2[perm] = vc
+    bt2 = np.where(bt >= 0, perm[np.maximum(bt, 0)], -1).astype(np.int32)
+    b = orc.decode(F32, q, kc2, vc2, bt2, cl, 0.3)
+    assert np.array_equal(a, b)
+    # contiguous layout: identity table over a pool filled in logical order
+    kc3 = np.zeros_like(kc)
+    vc3 = np.zeros_like(vc)
+    bt3 = np.full_like(bt, -1)
+    nxt = 0
+    for i, n in enumerate(lens):
+        for j in range(blocks_for_tokens(n, bs)):
+            kc3[nxt], vc3[nxt] = kc[bt[i, j]], vc[bt[i, j]]
+            bt3[i, j] = nxt
+            nxt += 1
+    c = orc.decode(F32, q, kc3, vc3, bt3, cl, 0.3)
+    assert np.array_equal(a, c)
+
+
+def check_gqa_equals_repeated_mha(orc, seed=32):
+    rng = np.random.default_rng(seed)
+    lens = [6, 10]
+    bs, nb, hkv, g, d = 4, 10, 2, 3, 8
+    kc, vc = _rand_pool(rng, nb, hkv, bs, d)
+    bt = _tables(rng, lens, bs, nb)
+    q = rng.standard_normal((2, hkv * g, d)).astype(np.float32)
+    cl = np.array(lens, np.int32)
+    a = orc.decode(F32, q, kc, vc, bt, cl, 0.5)
+    kr = np.ascontiguousarray(np.repeat(kc, g, axis=1))
+    vr = np.ascontiguousarray(np.repeat(vc, g, axis=1))
+    b = orc.decode(F32, q, kr, vr, bt, cl, 0.5)
+    assert np.array_equal(a, b)
+
+
+def check_decode_is_last_prefill_row(orc, seed=33):
+    rng = np.random.default_rng(seed)
+    prefix, chunk = [3, 0, 9], [2, 5, 1]
+    kc, vc, bt, cu_q, cu_k, q = _prefill_setup(rng, prefix, chunk, 4, 2, 8, 4)
+    out = orc.prefill(F32, q, kc, vc, bt, cu_q, cu_k, 0.6, causal=True)
+    last = cu_q[1:] - 1
+    lk = (cu_k[1:] - cu_k[:-1]).astype(np.int32)
+    dec = orc.decode(F32, q[last], kc, vc, bt, lk, 0.6)
+    assert np.array_equal(out[last], dec)
+
+
+def check_chunk_split_invariance(orc, seed=34):
+    """Prefill of (prefix P, chunk C) gives rows P..P+C-1 of one causal prefill over P + C tokens."""
+    rng = np.random.default_rng(seed)
+    p, c = 6, 5
+    kc, vc, bt, _, _, _ = _prefill_setup(rng, [p], [c], 2, 1, 8, 4)
+    q = rng.standard_normal((p + c, 2, 8)).astype(np.float32)
+    whole = orc.prefill(F32, q, kc, vc, bt, np.array([0, p + c], np.int32), np.array([0, p + c], np.int32),
+                        0.35, causal=True)
+    part = orc.prefill(F32, q[p:], kc, vc, bt, np.array([0, c], np.int32), np.array([0, p + c], np.int32),
+                       0.35, causal=True)
+    assert np.array_equal(whole[p:], part)
+
+
+def check_store_places_rows(orc, seed=41):
+    """Store then read back by numpy indexing of the [NB, Hkv, bs, D] layout; untouched rows keep
+    their sentinel; negative slots write nothing."""
+    rng = np.random.default_rng(seed)
+    nb, hkv, bs, d = 6, 3, 4, 5
+    kc = np.full((nb, hkv, bs, d), -7.0, np.float32)
+    vc = np.full((nb, hkv, bs, d), -9.0, np.float32)
+    slots = np.array([0, 23, 5, -1, 14], np.int32)
+    key = rng.standard_normal((5, hkv, d)).astype(np.float32)
+    val = rng.standard_normal((5, hkv, d)).astype(np.float32)
+    orc.store(F32, key, val, kc, vc, slots)
+    touched = np.zeros((nb, bs), bool)
+    for n, s in enumerate(slots):
+        if s < 0:
+            continue
+        assert np.array_equal(kc[s // bs, :, s % bs, :], key[n])
+        assert np.array_equal(vc[s // bs, :, s % bs, :], val[n])
+        touched[s // bs, s % bs] = True
+    assert np.all(kc.transpose(0, 2, 1, 3)[~touched] == -7.0)
+    assert np.all(vc.transpose(0, 2, 1, 3)[~touched] == -9.0)
+
+
+def check_gather_matches_numpy_indexing(orc, seed=42):
+    """Gather of logical tokens equals numpy indexing of the [NB, Hkv, bs, D] pool (several KV heads,
+    a ragged last block)."""
+    rng = np.random.default_rng(seed)
+    kc, vc = _rand_pool(rng, 9, 3, 4, 6)
+    bt = _tables(rng, [14], 4, 9)
+    ko, vo = orc.gather(F32, kc, vc, bt[0], 14)
+    assert np.array_equal(ko.astype(np.float64), numpy_gather(kc, bt[0], 14))
+    assert np.array_equal(vo.astype(np.float64), numpy_gather(vc, bt[0], 14))
+
+
+ALL_CHECKS = [
+    check_gather_matches_numpy_indexing,
+    check_single_key,
+    check_zero_query,
+    check_constant_values,
+    check_equal_keys,
+    check_two_keys_known_gap,
+    check_decode_vs_sdpa,
+    check_prefill_vs_sdpa,
+    check_block_permutation_invariance,
+    check_gqa_equals_repeated_mha,
+    check_decode_is_last_prefill_row,
+    check_chunk_split_invariance,
+    check_store_places_rows,
+]
