@@ -1,0 +1,211 @@
+"""Benchmark of the paged KV cache decode step on one MI355X.
+
+A step is one pass of the hot path over one batch: kv_cache_store of the batch's new token per
+sequence, then paged_attention_decode over every sequence's context (the split-K reduce included
+when a context spans several partitions). The default workload is batch 512 with context lengths
+lognormal (median 300, sigma 1) clipped to [16, 2048], block size 16, 32 query / 8 KV heads,
+head_dim 128, bf16, in a shuffled 80000-block pool.
+
+Inputs are resident in HBM before timing. Each step reads a different copy of the pool (R copies,
+R * step bytes >> the last-level cache), so K/V come from HBM, not from cache.
+
+Prints one JSON line (rank 0): value = algorithmic bytes of the step / step time (GB/s), plus the
+roofline of the decode call measured with HIP events on the launch stream, and the CPU oracle's rate
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+
+
+def decode_bytes(c) -> int:
+    """Algorithmic bytes of one decode call: K and V of every context token, q and out, the block-table
+    entries used and context_lens."""
+    e = 4 if c.dtype == "f32" else 2
+    lens = c.context_lens.astype(np.int64)
+    nb = -(-lens // c.block_size)
+    return int(2 * lens.sum() * c.num_kv_heads * c.head_dim * e + 2 * c.num_seqs * c.num_heads * c.head_dim * e
+               + 4 * nb.sum() + 4 * c.num_seqs)
+
+
+def store_bytes(c) -> int:
+    """Algorithmic bytes of one store call: read and write K and V rows of each new token, plus its slot."""
+    e = 4 if c.dtype == "f32" else 2
+    n = len(c.slot_mapping)
+    return int(n * c.num_kv_heads * c.head_dim * e * 2 * 2 + 4 * n)
+
+
+def cpu_baseline(c, target_s=12.0):
+    """Time the oracle (float64, all host cores) on a bounded sample of the same workload: the decode of
+    the whole batch, repeated until about target_s seconds of CPU work (fewer sequences if one pass is
+    already longer)."""
+    import oracle
+
+    orc = oracle.default()
+    kc, vc = c.pool.dense()
+    orc.store(c.dtype, c.key, c.value, kc, vc, c.slot_mapping)
+    order = np.random.default_rng(0).permutation(c.num_seqs)
+    probe = np.sort(order[:8]).astype(np.int32)
+    t0 = time.perf_counter()
+    orc.decode(c.dtype, c.query, kc, vc, c.block_tables, c.context_lens, c.scale, seqs=probe)
+    per_token = (time.perf_counter() - t0) / max(1, int(c.context_lens[probe].sum()))
+    total_tokens = int(c.context_lens.sum())
+    if per_token * total_tokens >= target_s:
+        cum = np.cumsum(c.context_lens[order])
+        k = max(8, min(c.num_seqs, int(np.searchsorted(cum, target_s / per_token)) + 1))
+        seqs, reps = np.sort(order[:k]).astype(np.int32), 1
+    else:
+        seqs, reps = None, max(1, int(round(target_s / max(per_token * total_tokens, 1e-9))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        orc.decode(c.dtype, c.query, kc, vc, c.block_tables, c.context_lens, c.scale, seqs=seqs)
+    dt = time.perf_counter() - t0
+    sel = np.arange(c.num_seqs) if seqs is None else seqs
+    e = 2 if c.dtype == "bf16" else 4
+    lens = c.context_lens[sel].astype(np.int64)
+    sample_bytes = reps * int(2 * lens.sum() * c.num_kv_heads * c.head_dim * e + 2 * len(sel) * c.num_heads
+                              * c.head_dim * e + 4 * (-(-lens // c.block_size)).sum() + 4 * len(sel))
+    return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(orc.max_threads()),
+            "kind": "oracle",
+            "sample": f"decode of {len(sel)} of {c.num_seqs} sequences ({int(lens.sum())} context tokens) x {reps} "
+                      f"passes, float64, {dt:.2f} s",
+            "seconds": round(dt, 3), "decode_tokens_per_s": round(reps * len(sel) / dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4], help="decode workload")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--copies", type=int, default=0, help="pool copies rotated per step (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_88_amd as pkv
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    pkv.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    c = W.make_config(args.config, args.seed)
+    td = torch.float32 if c.dtype == "f32" else torch.bfloat16
+
+    def tt(a):
+        a = np.ascontiguousarray(a)
+        if c.dtype == "f32":
+            return torch.from_numpy(a).to(dev)
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    step_bytes = decode_bytes(c) + store_bytes(c)
+    copies = args.copies or max(2, min(8, int(np.ceil(2.0e9 / max(step_bytes, 1)))))
+    shape = (c.num_blocks,) + c.pool.block_shape
+    idx = torch.from_numpy(c.pool.used_blocks.astype(np.int64)).to(dev)
+    kb, vb = tt(c.pool.key_blocks), tt(c.pool.value_blocks)
+    pools = []
+    for _ in range(copies):
+        kc = torch.full(shape, float("nan"), dtype=td, device=dev)
+        vc = torch.full(shape, float("nan"), dtype=td, device=dev)
+        kc.index_copy_(0, idx, kb)
+        vc.index_copy_(0, idx, vb)
+        pools.append((kc, vc))
+    del kb, vb
+    q, kn, vn = tt(c.query), tt(c.key), tt(c.value)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(c.block_tables).to(dev)
+    cl = torch.from_numpy(c.context_lens).to(dev)
+    sm = torch.from_numpy(c.slot_mapping).to(dev)
+    ws_n = pkv.decode_workspace_size(c.num_seqs, c.num_heads, c.num_kv_heads, c.head_dim, c.block_size,
+                                     c.max_context_len)
+    ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    n_ev = args.steps
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+
+    def step(k, timed=False):
+        kc, vc = pools[k % copies]
+        pkv.kv_cache_store(kn, vn, kc, vc, sm, stream=stream)
+        if timed:
+            ev0[k].record(stream)
+        pkv.paged_attention_decode(out, q, kc, vc, bt, cl, c.max_context_len, c.scale, workspace=ws, stream=stream)
+        if timed:
+            ev1[k].record(stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k, timed=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_ms = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)])
+    dec_avg_ms = float(dec_ms.mean())
+    achieved = decode_bytes(c) / (dec_avg_ms * 1e-3) / 1e9
+    finite = bool(torch.isfinite(out.float()).all().item())
+
+    result = {
+        "metric": "paged decode attention achieved HBM GB/s (% of peak) and decode tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "data": "synthetic",
+        "config": {"workload": c.name, "num_seqs": c.num_seqs, "context_lens": "lognormal median 300 sigma 1 clip [16, 2048]"
+                   if args.config == 3 else "see workloads", "sum_context_tokens": int(c.context_lens.sum()),
+                   "max_context_len": c.max_context_len, "block_size": c.block_size, "num_heads": c.num_heads,
+                   "num_kv_heads": c.num_kv_heads, "head_dim": c.head_dim, "num_blocks": c.num_blocks,
+                   "seed": c.seed, "pool_copies_rotated": copies},
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(c.num_seqs / (ms_per_step * 1e-3), 1),
+        "step_bytes": step_bytes,
+        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode call (decode_kernel + decode_reduce_kernel)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_ms": round(dec_avg_ms, 5), "algorithmic_bytes": decode_bytes(c)},
+        "outputs_finite": finite,
+        "gpu": torch.cuda.get_device_name(0),
+        "torch": torch.__version__,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(c)
+        result["cpu_baseline"]["host"] = platform.processor() or platform.machine()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * pagedkv.h -- C ABI of the MI355X (gfx950) paged KV cache library, libpagedkv.so.
+ *
+ * The library implements the hot path of a block-table paged KV cache:
+ *   pkv_kv_cache_store          scatter new K/V rows into their slots;
+ *   pkv_paged_attention_decode  one query token per sequence attends over its cached tokens;
+ *   pkv_paged_attention_prefill a varlen chunk of queries per sequence attends causally over its
+ *                               cached prefix plus the chunk;
+ *   pkv_kv_cache_gather         inverse of the store for one block table (test helper).
+ *
+ * Vocabulary (nano-vllm walkthrough, section 2 context: is_prefill, cu_seqlens_q/k, max_seqlen_q/k,
+ * slot_mapping, context_lens, block_tables; "推理运行时", section 分页 KV: logical block j of a
+ * request maps to physical block b_j through its block table):
+ *   block_size     tokens per physical block (a power of two, 1..256);
+ *   block_tables   int32 [num_seqs][block_table_stride]: entry j is the physical block that holds
+ *                  the sequence's logical tokens [j*block_size, (j+1)*block_size); entries past
+ *                  ceil(len / block_size) are never read (any value, e.g. -1);
+ *   slot           physical_block * block_size + offset_in_block, a flat token-row index;
+ *   context_lens   int32 [num_seqs]: tokens each decode query attends to, the token stored this
+ *                  step included ("LLM Infra 101 v0.2: KV Cache", section 推理);
+ *   cu_seqlens_q/k int32 [num_seqs + 1] prefix sums of the per-sequence query counts and key counts.
+ *
+ * Memory layout (all device memory, row-major, densely packed, 16-byte aligned):
+ *   key_cache, value_cache  [num_blocks][num_kv_heads][block_size][head_dim] of the dtype;
+ *   decode query / out      [num_seqs][num_heads][head_dim];
+ *   prefill query / out     [total_q][num_heads][head_dim], total_q = cu_seqlens_q[num_seqs];
+ *   new key / value rows    [num_tokens][num_kv_heads][head_dim].
+ * Query head h reads kv head h / (num_heads / num_kv_heads).
+ *
+ * Ownership and ordering: the caller owns every buffer; the library never allocates, frees or
+ * synchronises. Every call is enqueued on `stream` (0 = the null stream) and returns before the
+ * GPU work ends; ordering between calls is the caller's stream order (store before attention).
+ *
+ * Errors: a call returns PKV_OK or an error status and never aborts. Arguments known on the host
+ * are checked before any launch (PKV_EINVAL for null or misaligned pointers, negative or
+ * inconsistent sizes; PKV_EUNSUPPORTED for a head_dim, block_size or head grouping without a
+ * kernel; PKV_EWORKSPACE for a too-small workspace); nothing is launched on error. Launch failures
+ * return PKV_EHIP. pkv_last_error() gives the message of the calling thread's last error.
+ * Contents of device arrays (slot values, block ids, lengths) are preconditions, not checked:
+ * non-negative slots must be unique and < num_blocks * block_size; block ids read must lie in
+ * [0, num_blocks); 0 <= context_lens[i] <= max_context_len; cu_seqlens non-decreasing with
+ * per-sequence query count <= key count <= max_seqlen_k.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_EINVAL = 1,
+    PKV_EUNSUPPORTED = 2,
+    PKV_EWORKSPACE = 3,
+    PKV_EHIP = 4
+} pkv_status;
+
+/*
+ * kv_cache_store ("reshape_and_cache"). For each n in [0, num_tokens) with s = slot_mapping[n] >= 0,
+ * writes key[n] and value[n] ([num_kv_heads][head_dim] each) to row (s / block_size, :, s % block_size)
+ * of key_cache / value_cache; slots < 0 are padding and write nothing. A pure copy: bit-exact.
+ * Source: nano-vllm walkthrough, section 2 context (slot_mapping); Mini-SGLang 源码解析（二）,
+ * section 6.7 (out_loc, one allocated slot per new token, written into the page table) and
+ * section 7.2 (a spare page absorbs padding writes -- here a negative slot does).
+ * slot_mapping: device int32 [num_tokens]. num_blocks bounds the pool (used for validation of sizes).
+ */
+pkv_status pkv_kv_cache_store(pkv_dtype dtype, const void *key, const void *value, void *key_cache,
+                              void *value_cache, const int32_t *slot_mapping, int64_t num_tokens,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                              hipStream_t stream);
+
+/*
+ * Bytes of device workspace pkv_paged_attention_decode needs for these sizes (0: none). Long
+ * contexts are split into partitions whose partial softmax state (fp32 max, sum and head_dim
+ * accumulators per sequence, head and partition) is merged by a reduce pass.
+ */
+size_t pkv_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                                 int32_t head_dim, int32_t block_size, int32_t max_context_len);
+
+/*
+ * paged_attention_decode. For sequence i and query head h (kv head h / G, G = num_heads / num_kv_heads):
+ *   out[i][h] = sum_{t < context_lens[i]} softmax_t(scale * query[i][h] . K_i[t]) V_i[t],
+ * with K_i[t] = key_cache[block_tables[i][t / block_size]][h / G][t % block_size] and likewise V.
+ * A sequence with context_lens[i] == 0 gets zeros. fp32 data accumulates in fp32; bf16 data
+ * accumulates in fp32 and rounds the output to bf16 (nearest even).
+ * Source: "推理运行时", section 分页 KV (attention reads K/V through the block table);
+ * "LLM Infra 101 v0.2: KV Cache", section 推理 (decode attends to the cache plus the new token).
+ * block_tables: device int32 [num_seqs][block_table_stride]; context_lens: device int32 [num_seqs];
+ * max_context_len: host bound on context_lens (sizes the grid and the workspace), must be
+ * <= block_table_stride * block_size. workspace: device memory of at least
+ * pkv_paged_attention_decode_workspace_size(...) bytes (may be NULL when that is 0).
+ * head_dim in {64, 128}; num_heads / num_kv_heads in 1..8.
+ */
+pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *query, const void *key_cache,
+                                      const void *value_cache, const int32_t *block_tables,
+                                      int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
+                                      int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_attention_prefill (varlen, chunked). Sequence i owns query rows [cu_seqlens_q[i], cu_seqlens_q[i+1])
+ * (Lq rows) and has Lk = cu_seqlens_k[i+1] - cu_seqlens_k[i] tokens in the cache, the last Lq of
+ * which are this chunk (already stored); P = Lk - Lq is its cached prefix. Query row j of the chunk
+ * is position P + j; when causal it attends to logical tokens [0, P + j], else to [0, Lk).
+ * Same softmax, GQA mapping, block-table addressing and precision as decode (bf16 only: the
+ * products run on MFMA with bf16 operands and fp32 accumulation; the softmax weights are rounded
+ * to bf16 for the second product).
+ * Source: nano-vllm walkthrough, section 2 context (cu_seqlens_q/k, max_seqlen_q/k, block_tables);
+ * Mini-SGLang 源码解析（二）, sections 6.6 and 6.9 (a chunk extends cached_len by extend_len);
+ * "推理运行时", sections Chunked prefill and Prefill 与 decode 输入 (flattened tokens with
+ * per-sequence query ranges; chunked prefill has a cached history).
+ * cu_seqlens_q, cu_seqlens_k: device int32 [num_seqs + 1], starting at 0. max_seqlen_q and
+ * max_seqlen_k: host bounds on Lq and Lk (size the grid); max_seqlen_k <= block_table_stride * block_size.
+ * dtype must be PKV_BF16; head_dim 128; num_heads / num_kv_heads in 1..8.
+ */
+pkv_status pkv_paged_attention_prefill(pkv_dtype dtype, void *out, const void *query, const void *key_cache,
+                                       const void *value_cache, const int32_t *block_tables,
+                                       int32_t block_table_stride, const int32_t *cu_seqlens_q,
+                                       const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                                       int32_t max_seqlen_k, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                       int32_t causal, hipStream_t stream);
+
+/*
+ * kv_cache_gather: logical tokens [0, len) of one block table row into contiguous key_out /
+ * value_out [len][num_kv_heads][head_dim]; the inverse of the store, used to check it bit-exactly.
+ * Source: nano-vllm walkthrough, section 2 Sequence (token i of a sequence sits in block i / block_size).
+ * block_table_row: device int32 [ceil(len / block_size)].
+ */
+pkv_status pkv_kv_cache_gather(pkv_dtype dtype, void *key_out, void *value_out, const void *key_cache,
+                               const void *value_cache, const int32_t *block_table_row, int32_t len,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                               hipStream_t stream);
+
+/* Message of the calling thread's last non-OK status ("" if none). Owned by the library. */
+const char *pkv_last_error(void);
+
+/* Library version string. */
+const char *pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

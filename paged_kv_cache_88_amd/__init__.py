@@ -1,0 +1,183 @@
+"""MI355X paged KV cache: Python binding of libpagedkv.so (see include/pagedkv.h).
+
+This module only marshals arguments: it reads shapes from torch tensors, checks that they agree,
+passes raw device pointers and the current HIP stream to the C ABI and turns a non-OK status into an
+exception. Every step of the computation runs in the library's HIP kernels. There is no fallback:
+if the library is missing or no GPU is present, calls raise.
+
+Names match the C entry points without the ``pkv_`` prefix.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpagedkv.so")
+
+PKV_F32, PKV_BF16 = 0, 1
+STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP"}
+
+_lib = None
+
+
+class PagedKVError(ValueError):
+    """A non-OK status from the library; ``status`` holds its name."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = STATUS.get(status, status)
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpagedkv.so (torch's HIP runtime must be loaded first: it is, by ``import torch``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "pkv_kv_cache_store": [ctypes.c_int, P, P, P, P, P, I64, I32, I32, I32, I64, P],
+        "pkv_kv_cache_gather": [ctypes.c_int, P, P, P, P, P, I32, I32, I32, I32, I64, P],
+        "pkv_paged_attention_decode": [ctypes.c_int, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32, I64, F, P,
+                                       SZ, P],
+        "pkv_paged_attention_prefill": [ctypes.c_int, P, P, P, P, P, I32, P, P, I32, I32, I32, I32, I32, I32, I32,
+                                        I64, F, I32, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.pkv_paged_attention_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32]
+    lib.pkv_paged_attention_decode_workspace_size.restype = SZ
+    lib.pkv_last_error.restype = ctypes.c_char_p
+    lib.pkv_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise PagedKVError(rc, load_library().pkv_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def _i32(*ts):
+    for t in ts:
+        if t.dtype != torch.int32:
+            raise ValueError("index tensors must be int32")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def version() -> str:
+    return load_library().pkv_version().decode()
+
+
+def kv_cache_store(key, value, key_cache, value_cache, slot_mapping, stream=None):
+    """Scatter ``key``/``value`` [N, Hkv, D] into ``key_cache``/``value_cache`` [NB, Hkv, bs, D] at the
+    slots ``slot_mapping`` (int32 [N]; negative = skip)."""
+    lib = load_library()
+    _dev(key, value, key_cache, value_cache, slot_mapping)
+    _i32(slot_mapping)
+    nb, hkv, bs, d = key_cache.shape
+    n = key.shape[0]
+    if key.shape != (n, hkv, d) or value.shape != key.shape or value_cache.shape != key_cache.shape:
+        raise ValueError("key/value must be [N, Hkv, D] and both caches [NB, Hkv, bs, D]")
+    if slot_mapping.shape != (n,):
+        raise ValueError("slot_mapping must have one entry per token")
+    if not (key.dtype == value.dtype == key_cache.dtype == value_cache.dtype):
+        raise ValueError("key, value and caches must share a dtype")
+    _check(lib.pkv_kv_cache_store(_dtype_code(key), _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                  _ptr(slot_mapping), n, hkv, d, bs, nb, _stream(stream)))
+
+
+def kv_cache_gather(key_out, value_out, key_cache, value_cache, block_table_row, length, stream=None):
+    """Logical tokens [0, length) of one block table into ``key_out``/``value_out`` [length, Hkv, D]."""
+    lib = load_library()
+    _dev(key_out, value_out, key_cache, value_cache, block_table_row)
+    _i32(block_table_row)
+    nb, hkv, bs, d = key_cache.shape
+    if key_out.shape != (length, hkv, d) or value_out.shape != key_out.shape:
+        raise ValueError("outputs must be [length, Hkv, D]")
+    if block_table_row.numel() * bs < length:
+        raise ValueError("block_table_row too short for length")
+    _check(lib.pkv_kv_cache_gather(_dtype_code(key_cache), _ptr(key_out), _ptr(value_out), _ptr(key_cache),
+                                   _ptr(value_cache), _ptr(block_table_row), int(length), hkv, d, bs, nb,
+                                   _stream(stream)))
+
+
+def decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len) -> int:
+    return int(load_library().pkv_paged_attention_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                                        block_size, max_context_len))
+
+
+def paged_attention_decode(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len, scale,
+                           workspace=None, stream=None):
+    """Decode attention: ``out``/``query`` [B, Hq, D]; ``block_tables`` int32 [B, stride];
+    ``context_lens`` int32 [B]. ``workspace`` (uint8, device) is allocated here when None and needed."""
+    lib = load_library()
+    _dev(out, query, key_cache, value_cache, block_tables, context_lens, workspace)
+    _i32(block_tables, context_lens)
+    nb, hkv, bs, d = key_cache.shape
+    b, hq, d2 = query.shape
+    if d2 != d or out.shape != query.shape or value_cache.shape != key_cache.shape:
+        raise ValueError("query/out must be [B, Hq, D] with the caches' D")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or context_lens.shape != (b,):
+        raise ValueError("block_tables must be [B, stride] and context_lens [B]")
+    ws_need = decode_workspace_size(b, hq, hkv, d, bs, max_context_len)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=query.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pkv_paged_attention_decode(_dtype_code(query), _ptr(out), _ptr(query), _ptr(key_cache),
+                                          _ptr(value_cache), _ptr(block_tables), block_tables.shape[1],
+                                          _ptr(context_lens), b, int(max_context_len), hq, hkv, d, bs, nb, float(scale),
+                                          _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, cu_seqlens_q, cu_seqlens_k,
+                            max_seqlen_q, max_seqlen_k, scale, causal=True, stream=None):
+    """Varlen chunked prefill: ``out``/``query`` [total_q, Hq, D]; ``cu_seqlens_q/k`` int32 [B+1]."""
+    lib = load_library()
+    _dev(out, query, key_cache, value_cache, block_tables, cu_seqlens_q, cu_seqlens_k)
+    _i32(block_tables, cu_seqlens_q, cu_seqlens_k)
+    nb, hkv, bs, d = key_cache.shape
+    tq, hq, d2 = query.shape
+    b = cu_seqlens_q.shape[0] - 1
+    if d2 != d or out.shape != query.shape or value_cache.shape != key_cache.shape:
+        raise ValueError("query/out must be [total_q, Hq, D] with the caches' D")
+    if cu_seqlens_k.shape != cu_seqlens_q.shape or b < 0 or block_tables.dim() != 2 or block_tables.shape[0] != b:
+        raise ValueError("cu_seqlens_q/k must be [B+1] and block_tables [B, stride]")
+    _check(lib.pkv_paged_attention_prefill(_dtype_code(query), _ptr(out), _ptr(query), _ptr(key_cache),
+                                           _ptr(value_cache), _ptr(block_tables), block_tables.shape[1],
+                                           _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), b, int(max_seqlen_q),
+                                           int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), int(bool(causal)),
+                                           _stream(stream)))

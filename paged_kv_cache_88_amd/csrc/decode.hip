@@ -1,0 +1,411 @@
+// paged_attention_decode: one query token per sequence attends over the context_lens[i] tokens
+// that its block table points to (the token stored this step included).
+//
+// What is computed: for query head h of sequence i, kv head h / G (G = num_heads / num_kv_heads),
+//   out = sum_t softmax_t(scale * q . k_t) v_t over logical tokens t < context_lens[i],
+// where logical token t lives in physical block block_tables[i][t / block_size] at offset
+// t % block_size ("推理运行时", section 分页 KV: the block table maps logical to physical blocks
+// and the attention kernel reads K/V through it; "LLM Infra 101 v0.2: KV Cache", section 推理:
+// the new token attends to the cached tokens and itself). Decode is bound by reading the cache
+// (Mini-SGLang 源码解析（二）, section 8.3), so the kernel is built around streaming K/V once,
+// with enough bytes in flight to cover HBM latency.
+//
+// Work decomposition. The grid is (partition, kv head, sequence). A partition is a run of
+// part_tokens logical tokens (a multiple of block_size, spanning at most 64 blocks). A workgroup of
+// NW waves owns one (sequence, kv head, partition) and serves all G query heads of that kv head, so
+// every K/V byte is read once. If a sequence fits one partition the workgroup writes the final output;
+// otherwise it writes an unnormalised partial (running max m, sum l, accumulator o, fp32) and the
+// reduce kernel merges the partitions with the log-sum-exp rule.
+//
+// Inside a wave: LPT lanes share one token row (head_dim elements); each lane holds NV 16-byte
+// vectors of the row, so one load instruction covers RPW = 64 / LPT rows. A wave tile is R such
+// instructions (TILE = R * RPW tokens); tiles are dealt to the NW waves round-robin. Each wave runs a
+// two-stage software pipeline: the loads of its next tile are in flight while it computes the current
+// one. The partition's block-table slice (<= 64 ids) sits one id per lane in a register and is read
+// with a lane shuffle, so the only dependent memory round trip per tile is the K/V load itself.
+// Each LPT-lane group keeps its own online-softmax state (m, l, acc) for the G heads; groups, then
+// waves, are merged once at the end. q.k uses v_dot2_f32_bf16 on bf16 pairs (fp32 FMA for fp32 data);
+// the group sum is a DPP butterfly; softmax runs in log2 units (exp2 with scale*log2(e) folded in),
+// and the accumulator is rescaled only when some running max of the wave grows.
+#include "device_common.h"
+#include "launch.h"
+
+namespace pkv {
+
+constexpr int MAX_PART_BLOCKS = 64;           // block-table entries one partition may span
+constexpr float M_INIT = -1.0e30f;            // finite "minus infinity": keeps exp2(m - m') finite
+
+template <bool BF16, int D, int G, int NV_, int R_, int NW_>
+struct DecodeShape {
+    static constexpr int ES = BF16 ? 2 : 4;                     // element bytes
+    static constexpr int VEC = 16 / ES;                         // elements per 16-byte vector
+    static constexpr int VPR = D / VEC;                         // vectors per row
+    static constexpr int NV = NV_;                              // vectors per lane per row
+    static constexpr int LPT = VPR / NV;                        // lanes per token row
+    static constexpr int RPW = 64 / LPT;                        // rows per wave instruction
+    static constexpr int R = R_;                                // instructions per tile
+    static constexpr int TILE = R * RPW;                        // tokens per wave tile
+    static constexpr int EPL = NV * VEC;                        // elements per lane
+    static constexpr int NW = NW_;                              // waves per workgroup
+    static_assert(VPR % NV == 0 && LPT >= 1 && LPT <= 16 && (LPT & (LPT - 1)) == 0, "lanes per token");
+};
+
+template <class S>
+struct TileRegs {
+    u32x4 k[S::R][S::NV];
+    u32x4 v[S::R][S::NV];
+    bool valid[S::R];
+};
+
+template <bool BF16, int D, int G, int NV_, int R_, int NW_>
+__global__ void __launch_bounds__(64 * NW_)
+decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x4 *__restrict__ key_cache,
+              const u32x4 *__restrict__ value_cache, const int32_t *__restrict__ block_tables, int bt_stride,
+              const int32_t *__restrict__ context_lens, int max_context_len, int num_kv_heads,
+              int64_t num_blocks, int log2_bs, int part_tokens, float scale_log2e, float *__restrict__ ws_m,
+              float *__restrict__ ws_l, float *__restrict__ ws_o, int max_parts) {
+    using S = DecodeShape<BF16, D, G, NV_, R_, NW_>;
+    constexpr int NV = S::NV, LPT = S::LPT, RPW = S::RPW, R = S::R, TILE = S::TILE, EPL = S::EPL, VEC = S::VEC;
+    constexpr int NW = S::NW;
+
+    const int part = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = lane / LPT, sub = lane % LPT;
+    const int num_heads = num_kv_heads * G;
+
+    // context_lens first (an empty partition exits as soon as it arrives), then the partition's
+    // block-table slice, one id per lane, issued before waiting on the length
+    const int L = min(context_lens[seq], max_context_len);   // clamp keeps every read in bounds
+    const int first_blk = (part * part_tokens) >> log2_bs;
+    const int nbp = part_tokens >> log2_bs;
+    int my_blk = -1;
+    if (lane < nbp && first_blk + lane < bt_stride) my_blk = block_tables[(int64_t)seq * bt_stride + first_blk + lane];
+    const int nparts = (L + part_tokens - 1) / part_tokens;
+
+    if (L <= 0) {                                   // empty context: zeros (one workgroup writes)
+        if (part == 0) {
+            for (int idx = tid; idx < G * D; idx += 64 * NW) {
+                int64_t o = ((int64_t)seq * num_heads + kvh * G) * D + idx;
+                if constexpr (BF16) ((uint16_t *)out)[o] = 0; else ((float *)out)[o] = 0.f;
+            }
+        }
+        return;
+    }
+    if (part >= nparts) return;
+
+    const int start = part * part_tokens;
+    const int ntok = min(start + part_tokens, L) - start;
+    const int bs_mask = (1 << log2_bs) - 1;
+
+    // q for the G heads of this kv head: lane holds elements [(v * LPT + sub) * VEC, +VEC) of each
+    u32x4 q[G][NV];
+    {
+        const u32x4 *qv = (const u32x4 *)query;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                q[h][v] = qv[((int64_t)seq * num_heads + kvh * G + h) * S::VPR + v * LPT + sub];
+    }
+
+    // issue the loads of one tile (addresses clamped to a valid token; validity kept for masking)
+    auto issue = [&](int tile, TileRegs<S> &t) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int tl = tile * TILE + r * RPW + grp;
+            const bool in = tl < ntok;
+            const int tok = start + (in ? tl : 0);
+            const int64_t blk = __shfl(my_blk, (tok >> log2_bs) - first_blk);
+            t.valid[r] = in && blk >= 0 && blk < num_blocks;
+            const int64_t b = t.valid[r] ? blk : 0;
+            const int64_t base = (((b * num_kv_heads + kvh) << log2_bs) + (tok & bs_mask)) * S::VPR + sub;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                t.k[r][v] = key_cache[base + v * LPT];
+                t.v[r][v] = value_cache[base + v * LPT];
+            }
+        }
+    };
+
+    float m[G], l[G], acc[G][EPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = M_INIT;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+    }
+
+    auto compute = [&](int tile, TileRegs<S> &t) {
+        bool any_masked = false;
+#pragma unroll
+        for (int r = 0; r < R; ++r) any_masked |= !t.valid[r];
+        const bool partial = __builtin_amdgcn_ballot_w64(any_masked) != 0;   // wave-uniform
+        if (partial) {                                      // zero V of masked tokens (they may hold NaN)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+                    if (!t.valid[r]) t.v[r][v] = u32x4{0, 0, 0, 0};
+        }
+        float s[R][G];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float a = 0.f;
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if constexpr (BF16) a = dot2_bf16(q[h][v][j], t.k[r][v][j], a);
+                        else a = fmaf(__uint_as_float(q[h][v][j]), __uint_as_float(t.k[r][v][j]), a);
+                    }
+                a = group_sum<LPT>(a) * scale_log2e;
+                s[r][h] = (partial && !t.valid[r]) ? -INFINITY : a;
+            }
+        float m_new[G];
+        bool grow = false;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float mx = s[0][h];
+#pragma unroll
+            for (int r = 1; r < R; ++r) mx = fmaxf(mx, s[r][h]);
+            m_new[h] = fmaxf(m[h], mx);
+            grow |= m_new[h] > m[h];
+        }
+        if (__builtin_amdgcn_ballot_w64(grow)) {            // rescale only when a running max grew
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float alpha = fast_exp2(m[h] - m_new[h]);
+                m[h] = m_new[h];
+                l[h] *= alpha;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float vf[EPL];
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t w = t.v[r][v][j];
+                    if constexpr (BF16) {
+                        vf[v * VEC + 2 * j] = bf16_lo(w);
+                        vf[v * VEC + 2 * j + 1] = bf16_hi(w);
+                    } else {
+                        vf[v * VEC + j] = __uint_as_float(w);
+                    }
+                }
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float p = fast_exp2(s[r][h] - m[h]);
+                l[h] += p;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+            }
+        }
+    };
+
+    // two-stage pipeline over this wave's tiles: tile, tile + NW, tile + 2 NW, ...
+    const int ntiles = (ntok + TILE - 1) / TILE;
+    {
+        TileRegs<S> ta, tb;
+        int tile = wave;
+        if (tile < ntiles) issue(tile, ta);
+        while (tile < ntiles) {
+            const int n1 = tile + NW;
+            if (n1 < ntiles) issue(n1, tb);
+            compute(tile, ta);
+            if (n1 >= ntiles) break;
+            const int n2 = n1 + NW;
+            if (n2 < ntiles) issue(n2, ta);
+            compute(n1, tb);
+            tile = n2;
+        }
+    }
+
+    // merge the RPW groups of the wave (lanes with equal `sub` hold the same elements)
+#pragma unroll
+    for (int stride = LPT; stride < 64; stride *= 2) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float mo = __shfl_xor(m[h], stride);
+            const float lo = __shfl_xor(l[h], stride);
+            const float mn = fmaxf(m[h], mo);
+            const float a = fast_exp2(m[h] - mn), b = fast_exp2(mo - mn);
+            m[h] = mn;
+            l[h] = l[h] * a + lo * b;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] = acc[h][e] * a + __shfl_xor(acc[h][e], stride) * b;
+        }
+    }
+
+    if constexpr (NW > 1) {                           // merge the waves through LDS
+        __shared__ float s_m[NW][G];
+        __shared__ float s_l[NW][G];
+        __shared__ float s_o[NW][G][D];
+        if (grp == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                if (sub == 0) {
+                    s_m[wave][h] = m[h];
+                    s_l[wave][h] = l[h];
+                }
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) s_o[wave][h][(v * LPT + sub) * VEC + e] = acc[h][v * VEC + e];
+            }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < G * D; idx += 64 * NW) {
+            const int h = idx / D, d = idx % D;
+            float mm = s_m[0][h];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) mm = fmaxf(mm, s_m[w][h]);
+            float ll = 0.f, oo = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float f = fast_exp2(s_m[w][h] - mm);
+                ll += s_l[w][h] * f;
+                oo += s_o[w][h][d] * f;
+            }
+            const int head = kvh * G + h;
+            if (nparts == 1) {
+                const int64_t o = ((int64_t)seq * num_heads + head) * D + d;
+                if constexpr (BF16) ((uint16_t *)out)[o] = (uint16_t)f32_to_bf16_rne(oo / ll);
+                else ((float *)out)[o] = oo / ll;
+            } else {
+                const int64_t pidx = ((int64_t)seq * num_heads + head) * max_parts + part;
+                ws_o[pidx * D + d] = oo;
+                if (d == 0) {
+                    ws_m[pidx] = mm;
+                    ws_l[pidx] = ll;
+                }
+            }
+        }
+    } else {                                          // one wave: group 0 holds the result
+        if (grp != 0) return;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const int head = kvh * G + h;
+            if (nparts == 1) {
+                const float inv = 1.0f / l[h];
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    const int64_t o = ((int64_t)seq * num_heads + head) * D + (v * LPT + sub) * VEC;
+                    if constexpr (BF16) {
+                        u32x4 pk;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            pk[j] = f32_to_bf16_rne(acc[h][v * VEC + 2 * j] * inv) |
+                                    (f32_to_bf16_rne(acc[h][v * VEC + 2 * j + 1] * inv) << 16);
+                        *(u32x4 *)((uint16_t *)out + o) = pk;
+                    } else {
+                        *(f32x4 *)((float *)out + o) = f32x4{acc[h][v * VEC] * inv, acc[h][v * VEC + 1] * inv,
+                                                             acc[h][v * VEC + 2] * inv, acc[h][v * VEC + 3] * inv};
+                    }
+                }
+            } else {
+                const int64_t pidx = ((int64_t)seq * num_heads + head) * max_parts + part;
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+#pragma unroll
+                    for (int e = 0; e < VEC; e += 4)
+                        *(f32x4 *)&ws_o[pidx * D + (v * LPT + sub) * VEC + e] =
+                            f32x4{acc[h][v * VEC + e], acc[h][v * VEC + e + 1], acc[h][v * VEC + e + 2],
+                                  acc[h][v * VEC + e + 3]};
+                if (sub == 0) {
+                    ws_m[pidx] = m[h];
+                    ws_l[pidx] = l[h];
+                }
+            }
+        }
+    }
+}
+
+// Merge the partitions of each (sequence, head): M = max_p m_p, w_p = 2^(m_p - M),
+// out = sum_p w_p o_p / sum_p w_p l_p. One workgroup of D threads per (head, sequence).
+template <bool BF16, int D>
+__global__ void __launch_bounds__(D)
+decode_reduce_kernel(void *__restrict__ out, const int32_t *__restrict__ context_lens, int max_context_len,
+                     int num_heads, int part_tokens, const float *__restrict__ ws_m, const float *__restrict__ ws_l,
+                     const float *__restrict__ ws_o, int max_parts) {
+    const int head = blockIdx.x, seq = blockIdx.y, d = threadIdx.x;
+    const int L = min(context_lens[seq], max_context_len);
+    const int nparts = (L + part_tokens - 1) / part_tokens;
+    if (nparts <= 1) return;                         // written directly by the decode kernel
+    const int64_t pbase = ((int64_t)seq * num_heads + head) * max_parts;
+    float mm = M_INIT;
+    for (int p = 0; p < nparts; ++p) mm = fmaxf(mm, ws_m[pbase + p]);
+    float ll = 0.f, oo = 0.f;
+    for (int p = 0; p < nparts; ++p) {
+        const float f = fast_exp2(ws_m[pbase + p] - mm);
+        ll += ws_l[pbase + p] * f;
+        oo += ws_o[(pbase + p) * D + d] * f;
+    }
+    const float res = oo / ll;
+    const int64_t o = ((int64_t)seq * num_heads + head) * D + d;
+    if constexpr (BF16) ((uint16_t *)out)[o] = (uint16_t)f32_to_bf16_rne(res);
+    else ((float *)out)[o] = res;
+}
+
+template <bool BF16, int D, int G, int NV, int R, int NW>
+static hipError_t launch_decode_cfg(const DecodeArgs &a, hipStream_t stream) {
+    dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
+    hipLaunchKernelGGL((decode_kernel<BF16, D, G, NV, R, NW>), grid, dim3(64 * NW), 0, stream, a.out, a.query,
+                       (const u32x4 *)a.key_cache, (const u32x4 *)a.value_cache, a.block_tables, a.bt_stride,
+                       a.context_lens, a.max_context_len, a.num_kv_heads, a.num_blocks, a.log2_bs, a.part_tokens,
+                       a.scale_log2e, a.ws_m, a.ws_l, a.ws_o, a.num_parts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.num_parts <= 1) return e;
+    hipLaunchKernelGGL((decode_reduce_kernel<BF16, D>), dim3(a.num_kv_heads * G, a.num_seqs), dim3(D), 0, stream,
+                       a.out, a.context_lens, a.max_context_len, a.num_kv_heads * G, a.part_tokens, a.ws_m, a.ws_l,
+                       a.ws_o, a.num_parts);
+    return hipGetLastError();
+}
+
+// Kernel shape per (dtype, head_dim, group): vectors per lane NV, tile depth R, waves per workgroup NW.
+#ifndef PKV_DECODE_NW
+#define PKV_DECODE_NW 1
+#endif
+#ifndef PKV_DECODE_R2
+#define PKV_DECODE_R2 2      // tile depth when a lane holds two vectors of a row
+#endif
+template <bool BF16, int D, int G>
+static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
+    constexpr int VPR = D / (BF16 ? 8 : 4);
+    constexpr int NV = (VPR / ((G <= 4) ? 2 : 1) > 16) ? VPR / 16 : ((G <= 4) ? 2 : 1);
+    constexpr int R = (NV == 1) ? 2 * PKV_DECODE_R2 : (NV == 2 ? PKV_DECODE_R2 : 1);
+    return launch_decode_cfg<BF16, D, G, NV, R, PKV_DECODE_NW>(a, stream);
+}
+
+template <bool BF16, int D>
+static hipError_t launch_decode_d(const DecodeArgs &a, int group, hipStream_t stream) {
+    switch (group) {
+        case 1: return launch_decode_t<BF16, D, 1>(a, stream);
+        case 2: return launch_decode_t<BF16, D, 2>(a, stream);
+        case 3: return launch_decode_t<BF16, D, 3>(a, stream);
+        case 4: return launch_decode_t<BF16, D, 4>(a, stream);
+        case 5: return launch_decode_t<BF16, D, 5>(a, stream);
+        case 6: return launch_decode_t<BF16, D, 6>(a, stream);
+        case 7: return launch_decode_t<BF16, D, 7>(a, stream);
+        case 8: return launch_decode_t<BF16, D, 8>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode(const DecodeArgs &a, bool bf16, int head_dim, int group, hipStream_t stream) {
+    if (a.num_seqs == 0) return hipSuccess;
+    if (bf16) return head_dim == 128 ? launch_decode_d<true, 128>(a, group, stream)
+                                     : launch_decode_d<true, 64>(a, group, stream);
+    return head_dim == 128 ? launch_decode_d<false, 128>(a, group, stream)
+                           : launch_decode_d<false, 64>(a, group, stream);
+}
+
+int decode_max_part_blocks() { return MAX_PART_BLOCKS; }
+
+}  // namespace pkv

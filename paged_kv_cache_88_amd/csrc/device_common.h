@@ -1,0 +1,63 @@
+// Device-side helpers shared by the paged KV cache kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Cache layout: [num_blocks][num_kv_heads][block_size][head_dim]; the rows of one
+// (block, kv head) are contiguous, so a decode workgroup for one kv head streams whole
+// block_size x head_dim tiles.
+__device__ __forceinline__ int64_t cache_row(int64_t block, int kvh, int off, int num_kv_heads,
+                                             int block_size) {
+    return (block * num_kv_heads + kvh) * block_size + off;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// bf16 pair (packed in one dword) -> two floats, exact.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// dot of two bf16 pairs accumulated in fp32: acc + a.x*b.x + a.y*b.y (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
+                                           acc, false);
+}
+
+// DPP lane permutations inside a row of 16 lanes.
+// quad_perm [1,0,3,2] swaps neighbours, quad_perm [2,3,0,1] swaps pairs, row_half_mirror
+// reverses each 8-lane half, row_mirror reverses the 16-lane row. Applied in that order to a
+// sum, each step folds in a disjoint set of lanes, so after log2(n) steps every lane of an
+// aligned n-lane group holds the group total.
+enum : int { DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140 };
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over an aligned group of N lanes (N in {1, 2, 4, 8, 16}); every lane of the group gets it.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (N >= 2) v += dpp<DPP_XOR1>(v);
+    if constexpr (N >= 4) v += dpp<DPP_XOR2>(v);
+    if constexpr (N >= 8) v += dpp<DPP_HALF_MIRROR>(v);
+    if constexpr (N >= 16) v += dpp<DPP_MIRROR>(v);
+    return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pkv

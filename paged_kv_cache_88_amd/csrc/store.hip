@@ -1,0 +1,102 @@
+// kv_cache_store: scatter each new token's K and V rows into the slot named by slot_mapping,
+// and kv_cache_gather, its inverse for one block table (used to check the store bit-exactly).
+//
+// A slot is physical_block * block_size + offset (nano-vllm walkthrough, section 2 context,
+// slot_mapping; Mini-SGLang 源码解析（二）, section 6.7: out_loc allocated per new token and written
+// into the page table). The copy is a pure byte move, so the result is bit-exact.
+//
+// Work decomposition: one thread moves 16 bytes. A (token, kv head) row is head_dim * elem
+// bytes = CHUNKS 16-byte pieces; consecutive threads take consecutive pieces of the same row, so
+// each wave reads a contiguous run of the source and writes whole 128-byte lines of the cache.
+#include "device_common.h"
+#include "launch.h"
+
+namespace pkv {
+
+template <int CHUNKS>
+__global__ void __launch_bounds__(256) store_kernel(const u32x4 *__restrict__ key, const u32x4 *__restrict__ value,
+                                                    u32x4 *__restrict__ key_cache, u32x4 *__restrict__ value_cache,
+                                                    const int32_t *__restrict__ slot_mapping, int64_t num_rows,
+                                                    int num_kv_heads, int block_size, int num_blocks) {
+    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t row = gid / CHUNKS;            // row = token * num_kv_heads + kv head
+    if (row >= num_rows) return;
+    int chunk = (int)(gid % CHUNKS);
+    int64_t token = row / num_kv_heads;
+    int kvh = (int)(row % num_kv_heads);
+    int32_t slot = slot_mapping[token];
+    if (slot < 0) return;                  // padding token: nothing to write
+    if (slot / block_size >= num_blocks) return;   // outside the pool: precondition broken, skip
+    int64_t block = slot / block_size;
+    int off = slot % block_size;
+    int64_t dst = cache_row(block, kvh, off, num_kv_heads, block_size) * CHUNKS + chunk;
+    int64_t src = row * CHUNKS + chunk;
+    u32x4 k = __builtin_nontemporal_load(key + src);
+    u32x4 v = __builtin_nontemporal_load(value + src);
+    key_cache[dst] = k;
+    value_cache[dst] = v;
+}
+
+template <int CHUNKS>
+__global__ void __launch_bounds__(256) gather_kernel(u32x4 *__restrict__ key_out, u32x4 *__restrict__ value_out,
+                                                     const u32x4 *__restrict__ key_cache,
+                                                     const u32x4 *__restrict__ value_cache,
+                                                     const int32_t *__restrict__ block_table_row, int64_t num_rows,
+                                                     int num_kv_heads, int block_size, int num_blocks) {
+    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t row = gid / CHUNKS;            // row = token * num_kv_heads + kv head
+    if (row >= num_rows) return;
+    int chunk = (int)(gid % CHUNKS);
+    int64_t token = row / num_kv_heads;
+    int kvh = (int)(row % num_kv_heads);
+    int64_t block = block_table_row[token / block_size];
+    if (block < 0 || block >= num_blocks) {      // outside the pool: precondition broken, zeros
+        key_out[row * CHUNKS + chunk] = u32x4{0, 0, 0, 0};
+        value_out[row * CHUNKS + chunk] = u32x4{0, 0, 0, 0};
+        return;
+    }
+    int off = (int)(token % block_size);
+    int64_t src = cache_row(block, kvh, off, num_kv_heads, block_size) * CHUNKS + chunk;
+    key_out[row * CHUNKS + chunk] = key_cache[src];
+    value_out[row * CHUNKS + chunk] = value_cache[src];
+}
+
+hipError_t launch_store(const void *key, const void *value, void *key_cache, void *value_cache,
+                        const int32_t *slot_mapping, int64_t num_tokens, int num_kv_heads, int row_bytes,
+                        int block_size, int num_blocks, hipStream_t stream) {
+    int64_t rows = num_tokens * num_kv_heads;
+    int chunks = row_bytes / 16;
+    int64_t threads = rows * chunks;
+    if (threads == 0) return hipSuccess;
+    dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    auto k = (const u32x4 *)key, v = (const u32x4 *)value;
+    auto kc = (u32x4 *)key_cache, vc = (u32x4 *)value_cache;
+    switch (chunks) {
+        case 8: hipLaunchKernelGGL(store_kernel<8>, grid, block, 0, stream, k, v, kc, vc, slot_mapping, rows, num_kv_heads, block_size, num_blocks); break;
+        case 16: hipLaunchKernelGGL(store_kernel<16>, grid, block, 0, stream, k, v, kc, vc, slot_mapping, rows, num_kv_heads, block_size, num_blocks); break;
+        case 32: hipLaunchKernelGGL(store_kernel<32>, grid, block, 0, stream, k, v, kc, vc, slot_mapping, rows, num_kv_heads, block_size, num_blocks); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(void *key_out, void *value_out, const void *key_cache, const void *value_cache,
+                         const int32_t *block_table_row, int64_t len, int num_kv_heads, int row_bytes, int block_size,
+                         int num_blocks, hipStream_t stream) {
+    int64_t rows = len * num_kv_heads;
+    int chunks = row_bytes / 16;
+    int64_t threads = rows * chunks;
+    if (threads == 0) return hipSuccess;
+    dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    auto ko = (u32x4 *)key_out, vo = (u32x4 *)value_out;
+    auto kc = (const u32x4 *)key_cache, vc = (const u32x4 *)value_cache;
+    switch (chunks) {
+        case 8: hipLaunchKernelGGL(gather_kernel<8>, grid, block, 0, stream, ko, vo, kc, vc, block_table_row, rows, num_kv_heads, block_size, num_blocks); break;
+        case 16: hipLaunchKernelGGL(gather_kernel<16>, grid, block, 0, stream, ko, vo, kc, vc, block_table_row, rows, num_kv_heads, block_size, num_blocks); break;
+        case 32: hipLaunchKernelGGL(gather_kernel<32>, grid, block, 0, stream, ko, vo, kc, vc, block_table_row, rows, num_kv_heads, block_size, num_blocks); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace pkv

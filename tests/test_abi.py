@@ -1,0 +1,119 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/pagedkv.h declares, and its
+host-side argument checks reject bad calls before any GPU work (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+
+def declared_symbols():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_88_amd as m
+
+    return m
+
+
+@pytest.fixture(scope="module")
+def lib(pkv):
+    return pkv.load_library()
+
+
+def test_header_declares_entry_points():
+    syms = declared_symbols()
+    for name in ("pkv_kv_cache_store", "pkv_paged_attention_decode", "pkv_paged_attention_prefill",
+                 "pkv_kv_cache_gather", "pkv_paged_attention_decode_workspace_size", "pkv_last_error",
+                 "pkv_version"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_version(pkv):
+    assert "gfx950" in pkv.version()
+
+
+def _err(lib):
+    return lib.pkv_last_error().decode()
+
+
+FAKE = ctypes.c_void_p(1 << 20)     # never dereferenced: every call below fails validation first
+
+
+def test_store_validation(lib):
+    # head_dim 96 unsupported
+    assert lib.pkv_kv_cache_store(1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 96, 16, 8, None) == 2
+    assert "head_dim" in _err(lib)
+    # block size not a power of two
+    assert lib.pkv_kv_cache_store(1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 24, 8, None) == 2
+    # null pointer
+    assert lib.pkv_kv_cache_store(1, None, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 16, 8, None) == 1
+    # misaligned pointer
+    assert lib.pkv_kv_cache_store(1, ctypes.c_void_p((1 << 20) + 2), FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 16, 8, None) == 1
+    # bad dtype, negative count
+    assert lib.pkv_kv_cache_store(7, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 16, 8, None) == 1
+    assert lib.pkv_kv_cache_store(1, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 2, 128, 16, 8, None) == 1
+    # zero tokens is a no-op, even with null pointers
+    assert lib.pkv_kv_cache_store(1, None, None, None, None, None, 0, 2, 128, 16, 8, None) == 0
+
+
+def test_decode_validation(lib):
+    call = lib.pkv_paged_attention_decode
+    # heads not a multiple of kv heads
+    assert call(1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 10, 30, 4, 128, 16, 64, 0.1, None, 0, None) == 1
+    assert "multiple" in _err(lib)
+    # group of 16 unsupported
+    assert call(1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 10, 32, 2, 128, 16, 64, 0.1, None, 0, None) == 2
+    # max_context_len beyond the table
+    assert call(1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 65, 8, 2, 128, 16, 64, 0.1, None, 0, None) == 1
+    assert "exceeds" in _err(lib)
+    # workspace needed but missing
+    need = lib.pkv_paged_attention_decode_workspace_size(2, 8, 2, 128, 16, 4096)
+    assert need > 0
+    assert call(1, FAKE, FAKE, FAKE, FAKE, FAKE, 256, FAKE, 2, 4096, 8, 2, 128, 16, 4096, 0.1, None, 0, None) == 3
+    assert call(1, FAKE, FAKE, FAKE, FAKE, FAKE, 256, FAKE, 2, 4096, 8, 2, 128, 16, 4096, 0.1, FAKE, need - 1,
+                None) == 3
+    # non-finite scale
+    assert call(1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 10, 8, 2, 128, 16, 64, float("nan"), None, 0, None) == 1
+    # no sequences: no-op
+    assert call(1, None, None, None, None, None, 4, None, 0, 10, 8, 2, 128, 16, 64, 0.1, None, 0, None) == 0
+
+
+def test_decode_workspace_size(lib):
+    f = lib.pkv_paged_attention_decode_workspace_size
+    assert f(64, 32, 8, 128, 16, 512) == 0          # one partition: no workspace
+    assert f(16, 64, 8, 128, 256, 32768) >= 16 * 64 * 64 * 130 * 4
+
+
+def test_prefill_validation(lib):
+    call = lib.pkv_paged_attention_prefill
+    # fp32 prefill unsupported (MFMA path is bf16)
+    assert call(0, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 2, 8, 64, 8, 2, 128, 16, 64, 0.1, 1, None) == 2
+    # q longer than k
+    assert call(1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 2, 65, 64, 8, 2, 128, 16, 64, 0.1, 1, None) == 1
+    # k beyond table
+    assert call(1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 2, 8, 65, 8, 2, 128, 16, 64, 0.1, 1, None) == 1
+    # null cu_seqlens
+    assert call(1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, FAKE, 2, 8, 64, 8, 2, 128, 16, 64, 0.1, 1, None) == 1
+
+
+def test_binding_fails_loudly_without_library(pkv, tmp_path):
+    saved = pkv._lib
+    try:
+        pkv._lib = None
+        with pytest.raises(RuntimeError, match="missing"):
+            pkv.load_library(str(tmp_path / "nope.so"))
+    finally:
+        pkv._lib = saved
