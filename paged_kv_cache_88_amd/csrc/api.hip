@@ -83,7 +83,7 @@ struct DecodePlan {
     int part_tokens;
     int num_parts;
     size_t ws_bytes;
-    size_t off_l, off_o;
+    size_t off_items, off_m, off_l, off_o;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -95,9 +95,13 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim, in
     p.part_tokens = DECODE_PART < block_size * pkv::decode_max_part_blocks() ? DECODE_PART
                                                                              : block_size * pkv::decode_max_part_blocks();
     p.num_parts = max_context_len <= 0 ? 1 : (max_context_len + p.part_tokens - 1) / p.part_tokens;
+    // [ctrl: 256 B][work items: num_seqs * num_parts int2][partials when num_parts > 1]
+    p.off_items = 256;
+    p.ws_bytes = p.off_items + align256((size_t)num_seqs * p.num_parts * 8);
     if (p.num_parts > 1) {
         size_t n = (size_t)num_seqs * num_heads * p.num_parts;
-        p.off_l = align256(n * sizeof(float));
+        p.off_m = p.ws_bytes;
+        p.off_l = p.off_m + align256(n * sizeof(float));
         p.off_o = p.off_l + align256(n * sizeof(float));
         p.ws_bytes = p.off_o + n * head_dim * sizeof(float);
     }
@@ -179,12 +183,13 @@ pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *qu
     DecodePlan plan = plan_decode(num_seqs, num_heads, head_dim, block_size, max_context_len);
     REQUIRE(plan.part_tokens / block_size <= pkv::decode_max_part_blocks(), PKV_EUNSUPPORTED,
             "partition spans too many blocks");
-    REQUIRE(plan.num_parts <= 65535 * 1024, PKV_EINVAL, "max_context_len too large");
-    if (plan.ws_bytes > 0) {
-        REQUIRE(workspace != nullptr && workspace_bytes >= plan.ws_bytes, PKV_EWORKSPACE,
-                "decode needs %zu bytes of workspace (got %zu)", plan.ws_bytes, workspace_bytes);
-        REQUIRE(((uintptr_t)workspace & 255u) == 0, PKV_EINVAL, "workspace must be 256-byte aligned");
-    }
+    REQUIRE(plan.num_parts <= 32767, PKV_EINVAL, "max_context_len too large (at most 32767 partitions of %d tokens)",
+            plan.part_tokens);
+    REQUIRE((int64_t)num_seqs * plan.num_parts * num_kv_heads <= (int64_t)1 << 24, PKV_EINVAL,
+            "decode grid too large (num_seqs * partitions * num_kv_heads above 2^24)");
+    REQUIRE(workspace != nullptr && workspace_bytes >= plan.ws_bytes, PKV_EWORKSPACE,
+            "decode needs %zu bytes of workspace (got %zu)", plan.ws_bytes, workspace_bytes);
+    REQUIRE(((uintptr_t)workspace & 255u) == 0, PKV_EINVAL, "workspace must be 256-byte aligned");
     pkv::DecodeArgs a{};
     a.out = out;
     a.query = query;
@@ -201,8 +206,10 @@ pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *qu
     a.part_tokens = plan.part_tokens;
     a.num_parts = plan.num_parts;
     a.scale_log2e = scale * 1.4426950408889634f;
-    if (plan.ws_bytes > 0) {
-        a.ws_m = (float *)workspace;
+    a.ctrl = (int *)workspace;
+    a.items = (int2 *)((char *)workspace + plan.off_items);
+    if (plan.num_parts > 1) {
+        a.ws_m = (float *)((char *)workspace + plan.off_m);
         a.ws_l = (float *)((char *)workspace + plan.off_l);
         a.ws_o = (float *)((char *)workspace + plan.off_o);
     }

@@ -10,9 +10,12 @@
 // (Mini-SGLang 源码解析（二）, section 8.3), so the kernel is built around streaming K/V once,
 // with enough bytes in flight to cover HBM latency.
 //
-// Work decomposition. The grid is (partition, kv head, sequence). A partition is a run of
-// part_tokens logical tokens (a multiple of block_size, spanning at most 64 blocks). A workgroup of
-// NW waves owns one (sequence, kv head, partition) and serves all G query heads of that kv head, so
+// Work decomposition. A partition is a run of part_tokens logical tokens of one sequence (a multiple
+// of block_size, spanning at most 64 blocks). A one-workgroup plan kernel reads context_lens on the
+// device and writes the list of (sequence, partition) work items sorted longest first (a counting sort
+// on the partition's token count), so long partitions are dispatched first and the batch does not end
+// on a straggler. The decode grid is one workgroup per (work item, kv head) in that order; slots past
+// the item count exit at once. A workgroup of NW waves serves all G query heads of its kv head, so
 // every K/V byte is read once. If a sequence fits one partition the workgroup writes the final output;
 // otherwise it writes an unnormalised partial (running max m, sum l, accumulator o, fp32) and the
 // reduce kernel merges the partitions with the log-sum-exp rule.
@@ -57,44 +60,84 @@ struct TileRegs {
     bool valid[S::R];
 };
 
+constexpr int PLAN_THREADS = 1024;
+constexpr int PLAN_BUCKETS = 64;
+
+// Work list for the decode grid. items[k] = {seq | part << 16, ntok | (several partitions) << 31},
+// sorted by ntok descending in PLAN_BUCKETS buckets (order inside a bucket is arbitrary: every item
+// writes its own output, so the result does not depend on it). ctrl[0] = number of items.
+// Sequences with an empty context get zero outputs here. Single workgroup.
+__global__ void __launch_bounds__(PLAN_THREADS)
+decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int max_context_len, int part_tokens,
+                   int2 *__restrict__ items, int *__restrict__ ctrl, void *__restrict__ out, int out_row_elems,
+                   int elem_bytes) {
+    __shared__ int hist[PLAN_BUCKETS];
+    __shared__ int offs[PLAN_BUCKETS];
+    const int tid = threadIdx.x;
+    if (tid < PLAN_BUCKETS) hist[tid] = 0;
+    __syncthreads();
+    auto bucket = [&](int ntok) { return (int)(((int64_t)(part_tokens - ntok) * PLAN_BUCKETS) / part_tokens); };
+    for (int i = tid; i < num_seqs; i += PLAN_THREADS) {
+        const int L = min(context_lens[i], max_context_len);
+        for (int start = 0; start < L; start += part_tokens) atomicAdd(&hist[bucket(min(part_tokens, L - start))], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int b = 0; b < PLAN_BUCKETS; ++b) {
+            offs[b] = run;
+            run += hist[b];
+        }
+        ctrl[0] = run;
+    }
+    __syncthreads();
+    for (int i = tid; i < num_seqs; i += PLAN_THREADS) {
+        const int L = min(context_lens[i], max_context_len);
+        if (L <= 0) {                                 // empty context: zero outputs for every head
+            const int64_t n = (int64_t)out_row_elems * elem_bytes / 4;
+            uint32_t *o = (uint32_t *)((char *)out + (int64_t)i * out_row_elems * elem_bytes);
+            for (int64_t k = 0; k < n; ++k) o[k] = 0u;
+            continue;
+        }
+        const int multi = L > part_tokens ? (int)0x80000000u : 0;
+        for (int part = 0, start = 0; start < L; ++part, start += part_tokens) {
+            const int ntok = min(part_tokens, L - start);
+            const int pos = atomicAdd(&offs[bucket(ntok)], 1);
+            items[pos] = make_int2(i | (part << 16), ntok | multi);
+        }
+    }
+}
+
 template <bool BF16, int D, int G, int NV_, int R_, int NW_>
 __global__ void __launch_bounds__(64 * NW_)
 decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x4 *__restrict__ key_cache,
               const u32x4 *__restrict__ value_cache, const int32_t *__restrict__ block_tables, int bt_stride,
-              const int32_t *__restrict__ context_lens, int max_context_len, int num_kv_heads,
-              int64_t num_blocks, int log2_bs, int part_tokens, float scale_log2e, float *__restrict__ ws_m,
-              float *__restrict__ ws_l, float *__restrict__ ws_o, int max_parts) {
+              const int2 *__restrict__ items, const int *__restrict__ ctrl, int num_kv_heads, int64_t num_blocks,
+              int log2_bs, int part_tokens, float scale_log2e, float *__restrict__ ws_m, float *__restrict__ ws_l,
+              float *__restrict__ ws_o, int max_parts) {
     using S = DecodeShape<BF16, D, G, NV_, R_, NW_>;
     constexpr int NV = S::NV, LPT = S::LPT, RPW = S::RPW, R = S::R, TILE = S::TILE, EPL = S::EPL, VEC = S::VEC;
     constexpr int NW = S::NW;
 
-    const int part = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = lane / LPT, sub = lane % LPT;
     const int num_heads = num_kv_heads * G;
 
-    // context_lens first (an empty partition exits as soon as it arrives), then the partition's
-    // block-table slice, one id per lane, issued before waiting on the length
-    const int L = min(context_lens[seq], max_context_len);   // clamp keeps every read in bounds
-    const int first_blk = (part * part_tokens) >> log2_bs;
+    // work item in longest-first order; slots past the list exit
+    const int slot = blockIdx.x;
+    if (slot >= ctrl[0] * num_kv_heads) return;
+    const int2 item = items[slot / num_kv_heads];
+    const int kvh = slot % num_kv_heads;
+    const int seq = item.x & 0xffff, part = item.x >> 16;
+    const int ntok = item.y & 0x7fffffff;
+    const bool several = item.y < 0;
+
+    // the partition's block-table slice, one id per lane (partitions never pass the table's stride)
+    const int start = part * part_tokens;
+    const int first_blk = start >> log2_bs;
     const int nbp = part_tokens >> log2_bs;
     int my_blk = -1;
     if (lane < nbp && first_blk + lane < bt_stride) my_blk = block_tables[(int64_t)seq * bt_stride + first_blk + lane];
-    const int nparts = (L + part_tokens - 1) / part_tokens;
-
-    if (L <= 0) {                                   // empty context: zeros (one workgroup writes)
-        if (part == 0) {
-            for (int idx = tid; idx < G * D; idx += 64 * NW) {
-                int64_t o = ((int64_t)seq * num_heads + kvh * G) * D + idx;
-                if constexpr (BF16) ((uint16_t *)out)[o] = 0; else ((float *)out)[o] = 0.f;
-            }
-        }
-        return;
-    }
-    if (part >= nparts) return;
-
-    const int start = part * part_tokens;
-    const int ntok = min(start + part_tokens, L) - start;
     const int bs_mask = (1 << log2_bs) - 1;
 
     // q for the G heads of this kv head: lane holds elements [(v * LPT + sub) * VEC, +VEC) of each
@@ -274,7 +317,7 @@ decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x
                 oo += s_o[w][h][d] * f;
             }
             const int head = kvh * G + h;
-            if (nparts == 1) {
+            if (!several) {
                 const int64_t o = ((int64_t)seq * num_heads + head) * D + d;
                 if constexpr (BF16) ((uint16_t *)out)[o] = (uint16_t)f32_to_bf16_rne(oo / ll);
                 else ((float *)out)[o] = oo / ll;
@@ -292,7 +335,7 @@ decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const int head = kvh * G + h;
-            if (nparts == 1) {
+            if (!several) {
                 const float inv = 1.0f / l[h];
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
@@ -355,12 +398,17 @@ decode_reduce_kernel(void *__restrict__ out, const int32_t *__restrict__ context
 
 template <bool BF16, int D, int G, int NV, int R, int NW>
 static hipError_t launch_decode_cfg(const DecodeArgs &a, hipStream_t stream) {
-    dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
-    hipLaunchKernelGGL((decode_kernel<BF16, D, G, NV, R, NW>), grid, dim3(64 * NW), 0, stream, a.out, a.query,
-                       (const u32x4 *)a.key_cache, (const u32x4 *)a.value_cache, a.block_tables, a.bt_stride,
-                       a.context_lens, a.max_context_len, a.num_kv_heads, a.num_blocks, a.log2_bs, a.part_tokens,
-                       a.scale_log2e, a.ws_m, a.ws_l, a.ws_o, a.num_parts);
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, a.context_lens, a.num_seqs,
+                       a.max_context_len, a.part_tokens, a.items, a.ctrl, a.out, a.num_kv_heads * G * D,
+                       BF16 ? 2 : 4);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t slots = (int64_t)a.num_seqs * a.num_parts * a.num_kv_heads;
+    hipLaunchKernelGGL((decode_kernel<BF16, D, G, NV, R, NW>), dim3((unsigned)slots), dim3(64 * NW), 0, stream, a.out,
+                       a.query, (const u32x4 *)a.key_cache, (const u32x4 *)a.value_cache, a.block_tables,
+                       a.bt_stride, a.items, a.ctrl, a.num_kv_heads, a.num_blocks, a.log2_bs, a.part_tokens,
+                       a.scale_log2e, a.ws_m, a.ws_l, a.ws_o, a.num_parts);
+    e = hipGetLastError();
     if (e != hipSuccess || a.num_parts <= 1) return e;
     hipLaunchKernelGGL((decode_reduce_kernel<BF16, D>), dim3(a.num_kv_heads * G, a.num_seqs), dim3(D), 0, stream,
                        a.out, a.context_lens, a.max_context_len, a.num_kv_heads * G, a.part_tokens, a.ws_m, a.ws_l,

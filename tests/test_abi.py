@@ -93,8 +93,10 @@ def test_decode_validation(lib):
 
 def test_decode_workspace_size(lib):
     f = lib.pkv_paged_attention_decode_workspace_size
-    assert f(64, 32, 8, 128, 16, 512) == 0          # one partition: no workspace
-    assert f(16, 64, 8, 128, 256, 32768) >= 16 * 64 * 64 * 130 * 4
+    one = f(64, 32, 8, 128, 16, 512)                # one partition: control word + work list only
+    assert 0 < one < 4096
+    assert f(16, 64, 8, 128, 256, 32768) >= 16 * 64 * 32 * 130 * 4     # partials of 32 partitions
+    assert f(0, 32, 8, 128, 16, 512) == 0
 
 
 def test_prefill_validation(lib):
