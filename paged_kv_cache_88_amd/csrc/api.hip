@@ -88,16 +88,17 @@ struct DecodePlan {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size,
-                       int32_t max_context_len) {
+DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t max_context_len) {
     DecodePlan p{};
     // a partition spans at most decode_max_part_blocks() blocks (its table slice lives in one register)
     p.part_tokens = DECODE_PART < block_size * pkv::decode_max_part_blocks() ? DECODE_PART
                                                                              : block_size * pkv::decode_max_part_blocks();
     p.num_parts = max_context_len <= 0 ? 1 : (max_context_len + p.part_tokens - 1) / p.part_tokens;
-    // [ctrl: 256 B][work items: num_seqs * num_parts int2][partials when num_parts > 1]
+    // [ctrl: 256 B][work items: num_seqs * num_parts int4][partials when num_parts > 1]
+    (void)num_kv_heads;
     p.off_items = 256;
-    p.ws_bytes = p.off_items + align256((size_t)num_seqs * p.num_parts * 8);
+    p.ws_bytes = p.off_items + align256((size_t)num_seqs * p.num_parts * 16);
     if (p.num_parts > 1) {
         size_t n = (size_t)num_seqs * num_heads * p.num_parts;
         p.off_m = p.ws_bytes;
@@ -152,9 +153,8 @@ pkv_status pkv_kv_cache_gather(pkv_dtype dtype, void *key_out, void *value_out, 
 
 size_t pkv_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                                  int32_t head_dim, int32_t block_size, int32_t max_context_len) {
-    (void)num_kv_heads;
-    if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || log2_exact(block_size) < 0) return 0;
-    return plan_decode(num_seqs, num_heads, head_dim, block_size, max_context_len).ws_bytes;
+    if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || log2_exact(block_size) < 0) return 0;
+    return plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len).ws_bytes;
 }
 
 pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *query, const void *key_cache,
@@ -180,7 +180,7 @@ pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *qu
     REQUIRE(block_tables || max_context_len == 0, PKV_EINVAL, "null block_tables");
     REQUIRE(aligned16(out) && aligned16(query) && aligned16(key_cache) && aligned16(value_cache), PKV_EINVAL,
             "out, query and cache pointers must be 16-byte aligned");
-    DecodePlan plan = plan_decode(num_seqs, num_heads, head_dim, block_size, max_context_len);
+    DecodePlan plan = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len);
     REQUIRE(plan.part_tokens / block_size <= pkv::decode_max_part_blocks(), PKV_EUNSUPPORTED,
             "partition spans too many blocks");
     REQUIRE(plan.num_parts <= 32767, PKV_EINVAL, "max_context_len too large (at most 32767 partitions of %d tokens)",
@@ -207,7 +207,7 @@ pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *qu
     a.num_parts = plan.num_parts;
     a.scale_log2e = scale * 1.4426950408889634f;
     a.ctrl = (int *)workspace;
-    a.items = (int2 *)((char *)workspace + plan.off_items);
+    a.items = (int4 *)((char *)workspace + plan.off_items);
     if (plan.num_parts > 1) {
         a.ws_m = (float *)((char *)workspace + plan.off_m);
         a.ws_l = (float *)((char *)workspace + plan.off_l);

@@ -27,13 +27,18 @@
 // one. The partition's block-table slice (<= 64 ids) sits one id per lane in a register and is read
 // with a lane shuffle, so the only dependent memory round trip per tile is the K/V load itself.
 // Each LPT-lane group keeps its own online-softmax state (m, l, acc) for the G heads; groups, then
-// waves, are merged once at the end. q.k uses v_dot2_f32_bf16 on bf16 pairs (fp32 FMA for fp32 data);
-// the group sum is a DPP butterfly; softmax runs in log2 units (exp2 with scale*log2(e) folded in),
-// and the accumulator is rescaled only when some running max of the wave grows.
+// waves, are merged once at the end. For bf16 data both products use v_dot2_f32_bf16: q.k on bf16
+// pairs of the row, and p.v on the weights of two rows rounded to a bf16 pair (fp32 FMAs for fp32
+// data). The group sum is a DPP butterfly; softmax runs in log2 units (exp2 with scale*log2(e) folded
+// in), and the accumulator is rescaled only when some running max of the wave grows.
 #include "device_common.h"
 #include "launch.h"
 
 namespace pkv {
+
+#ifndef PKV_DECODE_NT
+#define PKV_DECODE_NT 1      // K/V loads are marked non-temporal: each byte is streamed once
+#endif
 
 constexpr int MAX_PART_BLOCKS = 64;           // block-table entries one partition may span
 constexpr float M_INIT = -1.0e30f;            // finite "minus infinity": keeps exp2(m - m') finite
@@ -51,6 +56,7 @@ struct DecodeShape {
     static constexpr int EPL = NV * VEC;                        // elements per lane
     static constexpr int NW = NW_;                              // waves per workgroup
     static_assert(VPR % NV == 0 && LPT >= 1 && LPT <= 16 && (LPT & (LPT - 1)) == 0, "lanes per token");
+    static_assert(!BF16 || R % 2 == 0, "bf16 p.v pairs rows: R must be even");
 };
 
 template <class S>
@@ -63,13 +69,13 @@ struct TileRegs {
 constexpr int PLAN_THREADS = 1024;
 constexpr int PLAN_BUCKETS = 64;
 
-// Work list for the decode grid. items[k] = {seq | part << 16, ntok | (several partitions) << 31},
-// sorted by ntok descending in PLAN_BUCKETS buckets (order inside a bucket is arbitrary: every item
-// writes its own output, so the result does not depend on it). ctrl[0] = number of items.
-// Sequences with an empty context get zero outputs here. Single workgroup.
+// Work list for the decode grid. items[k] = {seq, part, ntok, nparts}, sorted by ntok descending in
+// PLAN_BUCKETS buckets (order inside a bucket is arbitrary: every item writes its own output, so the
+// result does not depend on it). ctrl[0] = number of items. Sequences with an empty context get zero
+// outputs here. Single workgroup.
 __global__ void __launch_bounds__(PLAN_THREADS)
 decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int max_context_len, int part_tokens,
-                   int2 *__restrict__ items, int *__restrict__ ctrl, void *__restrict__ out, int out_row_elems,
+                   int4 *__restrict__ items, int *__restrict__ ctrl, void *__restrict__ out, int out_row_elems,
                    int elem_bytes) {
     __shared__ int hist[PLAN_BUCKETS];
     __shared__ int offs[PLAN_BUCKETS];
@@ -82,13 +88,16 @@ decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int m
         for (int start = 0; start < L; start += part_tokens) atomicAdd(&hist[bucket(min(part_tokens, L - start))], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int b = 0; b < PLAN_BUCKETS; ++b) {
-            offs[b] = run;
-            run += hist[b];
+    if (tid < 64) {                                   // exclusive scan of the 64 buckets in one wave
+        const int h = hist[tid];
+        int v = h;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(v, o);
+            if (tid >= o) v += u;
         }
-        ctrl[0] = run;
+        offs[tid] = v - h;
+        if (tid == 63) ctrl[0] = v;
     }
     __syncthreads();
     for (int i = tid; i < num_seqs; i += PLAN_THREADS) {
@@ -99,11 +108,11 @@ decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int m
             for (int64_t k = 0; k < n; ++k) o[k] = 0u;
             continue;
         }
-        const int multi = L > part_tokens ? (int)0x80000000u : 0;
+        const int nparts = (L + part_tokens - 1) / part_tokens;
         for (int part = 0, start = 0; start < L; ++part, start += part_tokens) {
             const int ntok = min(part_tokens, L - start);
             const int pos = atomicAdd(&offs[bucket(ntok)], 1);
-            items[pos] = make_int2(i | (part << 16), ntok | multi);
+            items[pos] = make_int4(i, part, ntok, nparts);
         }
     }
 }
@@ -112,9 +121,9 @@ template <bool BF16, int D, int G, int NV_, int R_, int NW_>
 __global__ void __launch_bounds__(64 * NW_)
 decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x4 *__restrict__ key_cache,
               const u32x4 *__restrict__ value_cache, const int32_t *__restrict__ block_tables, int bt_stride,
-              const int2 *__restrict__ items, const int *__restrict__ ctrl, int num_kv_heads, int64_t num_blocks,
-              int log2_bs, int part_tokens, float scale_log2e, float *__restrict__ ws_m, float *__restrict__ ws_l,
-              float *__restrict__ ws_o, int max_parts) {
+              const int4 *__restrict__ items, const int *__restrict__ ctrl, int num_kv_heads,
+              int64_t num_blocks, int log2_bs, int part_tokens, float scale_log2e,
+              float *__restrict__ ws_m, float *__restrict__ ws_l, float *__restrict__ ws_o, int max_parts) {
     using S = DecodeShape<BF16, D, G, NV_, R_, NW_>;
     constexpr int NV = S::NV, LPT = S::LPT, RPW = S::RPW, R = S::R, TILE = S::TILE, EPL = S::EPL, VEC = S::VEC;
     constexpr int NW = S::NW;
@@ -126,11 +135,10 @@ decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x
     // work item in longest-first order; slots past the list exit
     const int slot = blockIdx.x;
     if (slot >= ctrl[0] * num_kv_heads) return;
-    const int2 item = items[slot / num_kv_heads];
+    const int4 item = items[slot / num_kv_heads];
     const int kvh = slot % num_kv_heads;
-    const int seq = item.x & 0xffff, part = item.x >> 16;
-    const int ntok = item.y & 0x7fffffff;
-    const bool several = item.y < 0;
+    const int seq = item.x, part = item.y, ntok = item.z, nparts = item.w;
+    const bool several = nparts > 1;
 
     // the partition's block-table slice, one id per lane (partitions never pass the table's stride)
     const int start = part * part_tokens;
@@ -164,8 +172,13 @@ decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x
             const int64_t base = (((b * num_kv_heads + kvh) << log2_bs) + (tok & bs_mask)) * S::VPR + sub;
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
+#if PKV_DECODE_NT
+                t.k[r][v] = __builtin_nontemporal_load(key_cache + base + v * LPT);
+                t.v[r][v] = __builtin_nontemporal_load(value_cache + base + v * LPT);
+#else
                 t.k[r][v] = key_cache[base + v * LPT];
                 t.v[r][v] = value_cache[base + v * LPT];
+#endif
             }
         }
     };
@@ -191,6 +204,8 @@ decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x
                 for (int v = 0; v < NV; ++v)
                     if (!t.valid[r]) t.v[r][v] = u32x4{0, 0, 0, 0};
         }
+        // partial dot products of all (row, head) pairs first, then the group butterfly one step at a
+        // time over all of them: no DPP reads a value written by the instruction just before it
         float s[R][G];
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -204,7 +219,14 @@ decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x
                         if constexpr (BF16) a = dot2_bf16(q[h][v][j], t.k[r][v][j], a);
                         else a = fmaf(__uint_as_float(q[h][v][j]), __uint_as_float(t.k[r][v][j]), a);
                     }
-                a = group_sum<LPT>(a) * scale_log2e;
+                s[r][h] = a;
+            }
+        group_sum_all<LPT, R * G>(&s[0][0]);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float a = s[r][h] * scale_log2e;
                 s[r][h] = (partial && !t.valid[r]) ? -INFINITY : a;
             }
         float m_new[G];
@@ -227,27 +249,47 @@ decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x
                 for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
             }
         }
+        if constexpr (BF16) {
+            // bf16: weights of two rows rounded to a bf16 pair; V elements of the same dim of the two rows
+            // paired with v_perm; one v_dot2_f32_bf16 per (head, dim) covers both rows. The denominator
+            // sums the same rounded weights (dot with (1, 1)).
+            constexpr uint32_t ONES = 0x3f803f80u;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            float vf[EPL];
+            for (int r = 0; r < R; r += 2) {
+                uint32_t pp[G];
 #pragma unroll
-            for (int v = 0; v < NV; ++v)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t w = t.v[r][v][j];
-                    if constexpr (BF16) {
-                        vf[v * VEC + 2 * j] = bf16_lo(w);
-                        vf[v * VEC + 2 * j + 1] = bf16_hi(w);
-                    } else {
-                        vf[v * VEC + j] = __uint_as_float(w);
-                    }
+                for (int h = 0; h < G; ++h) {
+                    pp[h] = pack_bf16x2(fast_exp2(s[r][h] - m[h]), fast_exp2(s[r + 1][h] - m[h]));
+                    l[h] = dot2_bf16(pp[h], ONES, l[h]);
                 }
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float p = fast_exp2(s[r][h] - m[h]);
-                l[h] += p;
+                for (int v = 0; v < NV; ++v)
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t x = pair_lo(t.v[r][v][j], t.v[r + 1][v][j]);
+                        const uint32_t y = pair_hi(t.v[r][v][j], t.v[r + 1][v][j]);
+#pragma unroll
+                        for (int h = 0; h < G; ++h) {
+                            acc[h][v * VEC + 2 * j] = dot2_bf16(pp[h], x, acc[h][v * VEC + 2 * j]);
+                            acc[h][v * VEC + 2 * j + 1] = dot2_bf16(pp[h], y, acc[h][v * VEC + 2 * j + 1]);
+                        }
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float vf[EPL];
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) vf[v * VEC + j] = __uint_as_float(t.v[r][v][j]);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float p = fast_exp2(s[r][h] - m[h]);
+                    l[h] += p;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+                }
             }
         }
     };
@@ -371,29 +413,49 @@ decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x
 }
 
 // Merge the partitions of each (sequence, head): M = max_p m_p, w_p = 2^(m_p - M),
-// out = sum_p w_p o_p / sum_p w_p l_p. One workgroup of D threads per (head, sequence).
-template <bool BF16, int D>
-__global__ void __launch_bounds__(D)
+// out = sum_p w_p o_p / sum_p w_p l_p. One workgroup per (kv head, sequence) serves its G heads:
+// wave-level reductions give M and the denominator per head, then each thread merges (head, dim)
+// outputs with loads coalesced along dim. Sequences that fit one partition were written by the
+// decode kernel and exit at once.
+constexpr int REDUCE_THREADS = 256;
+
+template <bool BF16, int D, int G>
+__global__ void __launch_bounds__(REDUCE_THREADS)
 decode_reduce_kernel(void *__restrict__ out, const int32_t *__restrict__ context_lens, int max_context_len,
-                     int num_heads, int part_tokens, const float *__restrict__ ws_m, const float *__restrict__ ws_l,
+                     int num_kv_heads, int part_tokens, const float *__restrict__ ws_m, const float *__restrict__ ws_l,
                      const float *__restrict__ ws_o, int max_parts) {
-    const int head = blockIdx.x, seq = blockIdx.y, d = threadIdx.x;
+    __shared__ float s_max[G], s_inv[G];
+    const int kvh = blockIdx.x, seq = blockIdx.y;
     const int L = min(context_lens[seq], max_context_len);
     const int nparts = (L + part_tokens - 1) / part_tokens;
-    if (nparts <= 1) return;                         // written directly by the decode kernel
-    const int64_t pbase = ((int64_t)seq * num_heads + head) * max_parts;
-    float mm = M_INIT;
-    for (int p = 0; p < nparts; ++p) mm = fmaxf(mm, ws_m[pbase + p]);
-    float ll = 0.f, oo = 0.f;
-    for (int p = 0; p < nparts; ++p) {
-        const float f = fast_exp2(ws_m[pbase + p] - mm);
-        ll += ws_l[pbase + p] * f;
-        oo += ws_o[(pbase + p) * D + d] * f;
+    if (nparts <= 1) return;
+    const int num_heads = num_kv_heads * G;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int h = wave; h < G; h += REDUCE_THREADS / 64) {
+        const int64_t pbase = ((int64_t)seq * num_heads + kvh * G + h) * max_parts;
+        float mm = M_INIT;
+        for (int p = lane; p < nparts; p += 64) mm = fmaxf(mm, ws_m[pbase + p]);
+        for (int o = 32; o >= 1; o >>= 1) mm = fmaxf(mm, __shfl_xor(mm, o));
+        float ll = 0.f;
+        for (int p = lane; p < nparts; p += 64) ll += ws_l[pbase + p] * fast_exp2(ws_m[pbase + p] - mm);
+        for (int o = 32; o >= 1; o >>= 1) ll += __shfl_xor(ll, o);
+        if (lane == 0) {
+            s_max[h] = mm;
+            s_inv[h] = 1.0f / ll;
+        }
     }
-    const float res = oo / ll;
-    const int64_t o = ((int64_t)seq * num_heads + head) * D + d;
-    if constexpr (BF16) ((uint16_t *)out)[o] = (uint16_t)f32_to_bf16_rne(res);
-    else ((float *)out)[o] = res;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += REDUCE_THREADS) {
+        const int h = idx / D, d = idx % D;
+        const int64_t pbase = ((int64_t)seq * num_heads + kvh * G + h) * max_parts;
+        const float mm = s_max[h];
+        float oo = 0.f;
+        for (int p = 0; p < nparts; ++p) oo += ws_o[(pbase + p) * D + d] * fast_exp2(ws_m[pbase + p] - mm);
+        const float res = oo * s_inv[h];
+        const int64_t o = ((int64_t)seq * num_heads + kvh * G + h) * D + d;
+        if constexpr (BF16) ((uint16_t *)out)[o] = (uint16_t)f32_to_bf16_rne(res);
+        else ((float *)out)[o] = res;
+    }
 }
 
 template <bool BF16, int D, int G, int NV, int R, int NW>
@@ -410,8 +472,8 @@ static hipError_t launch_decode_cfg(const DecodeArgs &a, hipStream_t stream) {
                        a.scale_log2e, a.ws_m, a.ws_l, a.ws_o, a.num_parts);
     e = hipGetLastError();
     if (e != hipSuccess || a.num_parts <= 1) return e;
-    hipLaunchKernelGGL((decode_reduce_kernel<BF16, D>), dim3(a.num_kv_heads * G, a.num_seqs), dim3(D), 0, stream,
-                       a.out, a.context_lens, a.max_context_len, a.num_kv_heads * G, a.part_tokens, a.ws_m, a.ws_l,
+    hipLaunchKernelGGL((decode_reduce_kernel<BF16, D, G>), dim3(a.num_kv_heads, a.num_seqs), dim3(REDUCE_THREADS), 0,
+                       stream, a.out, a.context_lens, a.max_context_len, a.num_kv_heads, a.part_tokens, a.ws_m, a.ws_l,
                        a.ws_o, a.num_parts);
     return hipGetLastError();
 }

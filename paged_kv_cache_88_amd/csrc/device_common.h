@@ -22,13 +22,21 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float -> bf16 bits, round to nearest even (NaN stays NaN).
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32; NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    bf16x2_t r = {(__bf16)f, (__bf16)0.0f};
+    return __builtin_bit_cast(uint32_t, r) & 0xffffu;
 }
+
+// two floats -> packed bf16 pair (lo = a, hi = b), round to nearest even, one instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2_t r = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// (lo16(w0), lo16(w1)) and (hi16(w0), hi16(w1)): the same element of two bf16 pairs side by side.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t w0, uint32_t w1) { return __builtin_amdgcn_perm(w1, w0, 0x05040100u); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t w0, uint32_t w1) { return __builtin_amdgcn_perm(w1, w0, 0x07060302u); }
 
 // dot of two bf16 pairs accumulated in fp32: acc + a.x*b.x + a.y*b.y (v_dot2_f32_bf16).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
@@ -56,6 +64,28 @@ __device__ __forceinline__ float group_sum(float v) {
     if constexpr (N >= 8) v += dpp<DPP_HALF_MIRROR>(v);
     if constexpr (N >= 16) v += dpp<DPP_MIRROR>(v);
     return v;
+}
+
+// group_sum over K independent values, step-major: each butterfly step is applied to all K values
+// before the next, so a DPP never reads the result of the instruction right before it (no wait states).
+template <int N, int K>
+__device__ __forceinline__ void group_sum_all(float *v) {
+    if constexpr (N >= 2) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] += dpp<DPP_XOR1>(v[k]);
+    }
+    if constexpr (N >= 4) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] += dpp<DPP_XOR2>(v[k]);
+    }
+    if constexpr (N >= 8) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] += dpp<DPP_HALF_MIRROR>(v[k]);
+    }
+    if constexpr (N >= 16) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] += dpp<DPP_MIRROR>(v[k]);
+    }
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -32,7 +32,7 @@ struct DecodeArgs {
     int part_tokens;       // tokens per partition, a multiple of the block size
     int num_parts;         // ceil(max_context_len / part_tokens), >= 1
     float scale_log2e;
-    int2 *items;           // work list, [num_seqs * num_parts]
+    int4 *items;           // work list, [num_seqs * num_parts]
     int *ctrl;             // ctrl[0] = number of work items
     float *ws_m;           // [num_seqs][num_heads][num_parts]   (used when num_parts > 1)
     float *ws_l;           // [num_seqs][num_heads][num_parts]
