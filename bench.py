@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+MFMA_BF16_PEAK = 2.5e15     # MI355X dense bf16 MFMA, published
 
 
 def decode_bytes(c) -> int:
@@ -84,6 +85,61 @@ def cpu_baseline(c, target_s=12.0):
             "seconds": round(dt, 3), "decode_tokens_per_s": round(reps * len(sel) / dt, 3)}
 
 
+def prefill_flops(c) -> int:
+    """Algorithmic flops of one causal chunked-prefill call: 2 flops per multiply-add of QK^T and of PV over
+    the visible (query, key) pairs only; softmax not counted."""
+    p = c.prefix_lens.astype(np.int64)
+    q = c.chunk_lens.astype(np.int64)
+    pairs = int((q * p + q * (q + 1) // 2).sum()) if c.causal else int((q * (p + q)).sum())
+    return 4 * c.head_dim * c.num_heads * pairs
+
+
+def bench_prefill(pkv, torch, dev, iters=20):
+    """Chunked prefill (32 sequences, prefix U[0, 2048] + chunk U[64, 512], block 256, 32/8 heads, bf16):
+    store of the chunk then causal prefill, timed with HIP events on the launch stream."""
+    import workloads as W
+
+    c = W.chunked_prefill()
+
+    def tt(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    shape = (c.num_blocks,) + c.pool.block_shape
+    idx = torch.from_numpy(c.pool.used_blocks.astype(np.int64)).to(dev)
+    kc = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    vc = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    kc.index_copy_(0, idx, tt(c.pool.key_blocks))
+    vc.index_copy_(0, idx, tt(c.pool.value_blocks))
+    q, kn, vn = tt(c.query), tt(c.key), tt(c.value)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(c.block_tables).to(dev)
+    cq, ck = torch.from_numpy(c.cu_seqlens_q).to(dev), torch.from_numpy(c.cu_seqlens_k).to(dev)
+    sm = torch.from_numpy(c.slot_mapping).to(dev)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for k in range(iters + 3):
+        e = ev[k - 3] if k >= 3 else None
+        if e:
+            e[0].record(stream)
+        pkv.kv_cache_store(kn, vn, kc, vc, sm, stream=stream)
+        if e:
+            e[1].record(stream)
+        pkv.paged_attention_prefill(out, q, kc, vc, bt, cq, ck, c.max_seqlen_q, c.max_seqlen_k, c.scale,
+                                    causal=True, stream=stream)
+        if e:
+            e[2].record(stream)
+    torch.cuda.synchronize()
+    st_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    pf_ms = float(np.mean([b.elapsed_time(d) for _, b, d in ev]))
+    fl = prefill_flops(c)
+    return {"workload": c.name, "total_q": c.total_q, "prefill_ms": round(pf_ms, 5), "store_ms": round(st_ms, 5),
+            "gflop": round(fl / 1e9, 2), "tflops": round(fl / (pf_ms * 1e-3) / 1e12, 2),
+            "mfma_utilization": round(fl / (pf_ms * 1e-3) / MFMA_BF16_PEAK, 4), "peak_tflops": MFMA_BF16_PEAK / 1e12,
+            "store_gbs": round(store_bytes(c) / (st_ms * 1e-3) / 1e9, 1),
+            "outputs_finite": bool(torch.isfinite(out.float()).all().item())}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,6 +149,7 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--copies", type=int, default=0, help="pool copies rotated per step (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -201,6 +258,9 @@ def main():
         "gpu": torch.cuda.get_device_name(0),
         "torch": torch.__version__,
     }
+    if not args.no_prefill:
+        del pools
+        result["prefill"] = bench_prefill(pkv, torch, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(c)
         result["cpu_baseline"]["host"] = platform.processor() or platform.machine()

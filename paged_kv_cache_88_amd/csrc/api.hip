@@ -245,6 +245,8 @@ pkv_status pkv_paged_attention_prefill(pkv_dtype dtype, void *out, const void *q
             "null pointer argument");
     REQUIRE(aligned16(out) && aligned16(query) && aligned16(key_cache) && aligned16(value_cache), PKV_EINVAL,
             "out, query and cache pointers must be 16-byte aligned");
+    REQUIRE((int64_t)num_seqs * num_kv_heads * ((max_seqlen_q + 15) / 16 + 8) <= ((int64_t)1 << 26), PKV_EINVAL,
+            "prefill grid too large");
     pkv::PrefillArgs a{};
     a.out = out;
     a.query = query;

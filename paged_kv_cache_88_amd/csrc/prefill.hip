@@ -11,25 +11,35 @@
 // Prefill is bound by compute (Mini-SGLang 源码解析（二）, section 8.3), so both products run on
 // MFMA: v_mfma_f32_16x16x32_bf16, bf16 operands, fp32 accumulation.
 //
-// Work decomposition. Grid (query tile, kv head, sequence). A 256-thread workgroup (4 waves) owns
+// Work decomposition. One workgroup per (sequence, kv head, query tile). Workgroups are dealt to the
+// 8 XCDs round-robin by their linear id, so the id is remapped to keep every query tile of one
+// (sequence, kv head) on the same XCD, dispatched back to back (the heaviest, last tile first): the
+// K/V rows they all read then come from that XCD's L2 instead of being fetched once per tile.
+// A 256-thread workgroup (4 waves) owns
 // 128 "rows" = BQ query positions x the G query heads that share the kv head (row = pos * G + h),
-// so each K/V tile brought into LDS serves all G heads. Each wave owns 32 rows (two 16-row MFMA
-// blocks). The key loop walks 64-key tiles up to the last key any row of the tile may see:
-//   1. the workgroup gathers the tile's K rows (row-major) and V rows (transposed, key-contiguous)
-//      from their physical blocks into LDS;
-//   2. S = Q K^T on MFMA (Q stays in registers as the A operand);
-//   3. mask (causal, bottom-right aligned, and the sequence end), online softmax per row in log2
-//      units with a 16-lane DPP max; P is rounded to bf16 and staged in LDS to become an A operand;
-//   4. O += P V on MFMA with V^T from LDS as the B operand.
+// so each K/V tile brought into LDS serves all G heads. Each wave owns 32 rows. The key loop walks
+// 64-key tiles up to the last key any row of the tile may see; the next tile's K/V rows are loaded
+// into registers while the current tile is computed.
+//   - Gather: K rows go to LDS row-major; each thread transposes a 4-key x 8-dim piece of V in
+//     registers (v_perm) and stores it key-contiguous, so LDS holds V^T.
+//   - S^T = K Q^T on MFMA: K (LDS) is the A operand, Q (registers) the B operand. In the 16x16
+//     output block lane l holds keys 4*(l/16)+i of query row l%16.
+//   - Mask (causal, bottom-right aligned; sequence end), online softmax per query row in log2 units:
+//     a row's 64 scores sit in 16 values of each of 4 lanes (lane, lane^16, lane^32, lane^48).
+//   - O^T += V^T P^T on MFMA: the rounded weights of S^T's registers are already laid out as the B
+//     operand (a lane's 8 reduction elements are keys {4b..4b+3} and {16+4b..16+4b+3} of a 32-key
+//     step, b = l/16), and V^T is read from LDS with the same key order as the A operand. P never
+//     goes through LDS.
 // The MFMA output layout is the 16x16 fp32 block with lane l holding rows 4*(l/16)+i, column l%16;
-// the A/B operands take 8 consecutive bf16 of the reduction index per lane, the same rule for both
-// operands, so any reduction order the hardware uses pairs matching elements.
+// the A/B operands take 8 reduction elements per lane, paired between the operands element by
+// element, so any reduction order of the hardware sums matching pairs.
 #include "device_common.h"
 #include "launch.h"
 
 namespace pkv {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int PF_THREADS = 256;
 constexpr int PF_D = 128;
@@ -37,43 +47,35 @@ constexpr int PF_BN = 64;                 // keys per tile
 constexpr int PF_ROWS = 128;              // rows per workgroup
 constexpr int PF_WROWS = 32;              // rows per wave
 constexpr int PF_KPAD = PF_D + 8;         // LDS row stride of K, bf16 elements (272 bytes)
-constexpr int PF_VPAD = PF_BN + 8;        // LDS row stride of V^T (144 bytes)
-constexpr int PF_PPAD = PF_BN + 8;        // LDS row stride of P (144 bytes)
+constexpr int PF_VPAD = PF_BN + 4;        // LDS row stride of V^T (136 bytes: 16 rows fall on distinct bank pairs)
 constexpr float PF_M_INIT = -1.0e30f;
+constexpr int PF_XCDS = 8;                // MI355X: 8 XCDs, each with its own L2
 
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                    c, 0, 0, 0);
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dppf(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ float row16_max(float v) {
-    v = fmaxf(v, dppf<DPP_XOR1>(v));
-    v = fmaxf(v, dppf<DPP_XOR2>(v));
-    v = fmaxf(v, dppf<DPP_HALF_MIRROR>(v));
-    v = fmaxf(v, dppf<DPP_MIRROR>(v));
-    return v;
-}
-
 template <int G>
-__global__ void __launch_bounds__(PF_THREADS)
+__global__ void __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, const u32x4 *__restrict__ key_cache,
                const u32x4 *__restrict__ value_cache, const int32_t *__restrict__ block_tables, int bt_stride,
-               const int32_t *__restrict__ cu_seqlens_q, const int32_t *__restrict__ cu_seqlens_k, int max_seqlen_k,
-               int num_kv_heads, int64_t num_blocks, int log2_bs, float scale_log2e, int causal) {
+               const int32_t *__restrict__ cu_seqlens_q, const int32_t *__restrict__ cu_seqlens_k, int num_seqs,
+               int max_seqlen_k, int num_q_tiles, int num_kv_heads, int64_t num_blocks, int log2_bs, float scale_log2e,
+               int causal) {
     constexpr int BQ = PF_ROWS / G;           // query positions per workgroup
     constexpr int VR = BQ * G;                // rows in use (<= 128)
     constexpr int CH = PF_D / 8;              // 16-byte chunks per K/V row
 
     __shared__ __attribute__((aligned(16))) uint16_t sK[PF_BN * PF_KPAD];
     __shared__ __attribute__((aligned(16))) uint16_t sV[PF_D * PF_VPAD];
-    __shared__ __attribute__((aligned(16))) uint16_t sP[PF_THREADS / 64][PF_WROWS * PF_PPAD];
 
-    const int qt = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
+    // linear id w runs on XCD w % 8: group g = (sequence, kv head) lives on XCD g % 8
+    const int w = blockIdx.x, xcd = w & (PF_XCDS - 1), j = w / PF_XCDS;
+    const int g = (j / num_q_tiles) * PF_XCDS + xcd;
+    if (g >= num_seqs * num_kv_heads) return;
+    const int qt = num_q_tiles - 1 - j % num_q_tiles;
+    const int seq = g / num_kv_heads, kvh = g % num_kv_heads;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lb = lane >> 4;       // MFMA lane row / lane block
     const int num_heads = num_kv_heads * G;
@@ -87,140 +89,209 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
     const int npos = min(BQ, Lq - pos0);
     const int kend = causal ? min(Lk, P + pos0 + npos) : Lk;   // keys [0, kend) may be visible
     const int ntiles = (kend + PF_BN - 1) / PF_BN;
+    const int kfull = causal ? P + pos0 + 1 : Lk;              // keys [0, kfull) visible to every row
     const int bs_mask = (1 << log2_bs) - 1;
     const int32_t *bt = block_tables + (int64_t)seq * bt_stride;
 
-    // Q operand: this lane supplies row (wave*32 + rb*16 + lr), dims 8*lb + 32*ks .. +8
-    u32x4 qa[2][4];
+    // this lane's two query rows (one per 16-row block qb): row = wave*32 + 16*qb + lr
+    int kmax[2];
+    bool row_ok[2];
+    u32x4 qb_reg[2][4];                       // B operand of S^T: dims 8*lb + 32*ks .. +8 of the row
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int r = wave * PF_WROWS + rb * 16 + lr;
+    for (int qb = 0; qb < 2; ++qb) {
+        const int r = wave * PF_WROWS + qb * 16 + lr;
         const int pos = r / G, h = r % G;
-        const bool ok = r < VR && pos < npos;
-        const int64_t qrow = ((int64_t)(q0 + pos0 + (ok ? pos : 0)) * num_heads + kvh * G + h) * CH;
+        row_ok[qb] = r < VR && pos < npos;
+        kmax[qb] = causal ? P + pos0 + pos : Lk - 1;
+        const int64_t qrow = ((int64_t)(q0 + pos0 + (row_ok[qb] ? pos : 0)) * num_heads + kvh * G + h) * CH;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qa[rb][ks] = ok ? query[qrow + lb + 4 * ks] : u32x4{0, 0, 0, 0};
+        for (int ks = 0; ks < 4; ++ks) qb_reg[qb][ks] = row_ok[qb] ? query[qrow + lb + 4 * ks] : u32x4{0, 0, 0, 0};
     }
 
-    f32x4 o[2][8];
-    float m[2][4], l[2][4];
+    // gather roles: K chunks tid + 256*c (c < 4); V piece = keys 4*vkg..+4 x dims 8*vdg..+8, with the
+    // 16 lanes of a row group on consecutive key groups so their V^T stores fill 128 contiguous bytes
+    const int vkg = tid & 15, vdg = tid >> 4;
+    u32x4 kreg[4], vreg[4];
+    auto load_tile = [&](int key0) {
+        if (log2_bs >= 6 && key0 + PF_BN <= kend) {
+            // the whole tile lies in one block (64 | block_size, tiles start at multiples of 64)
+            const int64_t blk = bt[key0 >> log2_bs];
+            const bool ok = blk >= 0 && blk < num_blocks;
+            const int64_t base = ((((ok ? blk : 0) * num_kv_heads + kvh) << log2_bs) + (key0 & bs_mask)) * CH;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+            for (int c = 0; c < 4; ++c) {
+                const int idx = tid + c * PF_THREADS;
+                kreg[c] = ok ? key_cache[base + idx] : u32x4{0, 0, 0, 0};
+            }
 #pragma unroll
-        for (int db = 0; db < 8; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            m[rb][i] = PF_M_INIT;
-            l[rb][i] = 0.f;
+            for (int i = 0; i < 4; ++i) vreg[i] = ok ? value_cache[base + (vkg * 4 + i) * CH + vdg] : u32x4{0, 0, 0, 0};
+            return;
         }
-    }
-
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int key0 = kt * PF_BN;
-        // 1. gather the tile: 64 keys x 16 chunks; K row-major, V transposed
 #pragma unroll
-        for (int c = 0; c < (PF_BN * CH) / PF_THREADS; ++c) {
+        for (int c = 0; c < 4; ++c) {
             const int idx = tid + c * PF_THREADS;
-            const int key = idx / CH, ch = idx % CH;
-            const int gk = key0 + key;
-            u32x4 kv = u32x4{0, 0, 0, 0}, vv = u32x4{0, 0, 0, 0};
+            const int gk = key0 + idx / CH, ch = idx % CH;
+            kreg[c] = u32x4{0, 0, 0, 0};
             if (gk < kend) {
                 const int64_t blk = bt[gk >> log2_bs];
-                if (blk >= 0 && blk < num_blocks) {
-                    const int64_t row = ((blk * num_kv_heads + kvh) << log2_bs) + (gk & bs_mask);
-                    kv = key_cache[row * CH + ch];
-                    vv = value_cache[row * CH + ch];
-                }
-            }
-            *(u32x4 *)&sK[key * PF_KPAD + ch * 8] = kv;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                sV[(ch * 8 + 2 * j) * PF_VPAD + key] = (uint16_t)(vv[j] & 0xffffu);
-                sV[(ch * 8 + 2 * j + 1) * PF_VPAD + key] = (uint16_t)(vv[j] >> 16);
+                if (blk >= 0 && blk < num_blocks)
+                    kreg[c] = key_cache[(((blk * num_kv_heads + kvh) << log2_bs) + (gk & bs_mask)) * CH + ch];
             }
         }
-        __syncthreads();
-
-        // 2. S = Q K^T for this wave's 32 rows x 64 keys
-        f32x4 s[2][4];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            s[0][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            s[1][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const u32x4 kb = *(const u32x4 *)&sK[(nb * 16 + lr) * PF_KPAD + lb * 8 + ks * 32];
-                s[0][nb] = mfma16x16x32(qa[0][ks], kb, s[0][nb]);
-                s[1][nb] = mfma16x16x32(qa[1][ks], kb, s[1][nb]);
-            }
-        }
-
-        // 3. mask, online softmax, P -> LDS (bf16)
-        uint16_t *pw = sP[wave];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = wave * PF_WROWS + rb * 16 + lb * 4 + i;
-                const int pos = r / G;
-                const bool row_ok = r < VR && pos < npos;
-                const int kmax = causal ? P + pos0 + pos : Lk - 1;     // last visible key
-                float mx = -INFINITY;
-                float sv[4];
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    const int key = key0 + nb * 16 + lr;
-                    const bool ok = row_ok && key < kend && key <= kmax;
-                    sv[nb] = ok ? s[rb][nb][i] * scale_log2e : -INFINITY;
-                    mx = fmaxf(mx, sv[nb]);
-                }
-                mx = row16_max(mx);
-                const float m_new = fmaxf(m[rb][i], mx);
-                const float alpha = fast_exp2(m[rb][i] - m_new);
-                m[rb][i] = m_new;
-                float rs = 0.f;
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    const float p = fast_exp2(sv[nb] - m_new);
-                    const uint32_t pb = f32_to_bf16_rne(p);
-                    rs += __uint_as_float(pb << 16);        // sum the rounded weights the MFMA uses
-                    pw[(rb * 16 + lb * 4 + i) * PF_PPAD + nb * 16 + lr] = (uint16_t)pb;
-                }
-                l[rb][i] = l[rb][i] * alpha + rs;
-#pragma unroll
-                for (int db = 0; db < 8; ++db) o[rb][db][i] *= alpha;
-            }
-        }
-        __syncthreads();
-
-        // 4. O += P V
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const u32x4 pa0 = *(const u32x4 *)&pw[(0 * 16 + lr) * PF_PPAD + lb * 8 + ks * 32];
-            const u32x4 pa1 = *(const u32x4 *)&pw[(1 * 16 + lr) * PF_PPAD + lb * 8 + ks * 32];
-#pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                const u32x4 vb = *(const u32x4 *)&sV[(db * 16 + lr) * PF_VPAD + lb * 8 + ks * 32];
-                o[0][db] = mfma16x16x32(pa0, vb, o[0][db]);
-                o[1][db] = mfma16x16x32(pa1, vb, o[1][db]);
-            }
-        }
-        __syncthreads();
-    }
-
-    // normalise and write: lane holds rows 4*lb + i of each 16-row block, column lr of each 16-dim block
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float lsum = group_sum<16>(l[rb][i]);
-            const int r = wave * PF_WROWS + rb * 16 + lb * 4 + i;
-            const int pos = r / G, h = r % G;
-            if (r >= VR || pos >= npos) continue;
-            const float inv = 1.0f / lsum;
-            uint16_t *orow = out + ((int64_t)(q0 + pos0 + pos) * num_heads + kvh * G + h) * PF_D;
+            const int gk = key0 + vkg * 4 + i;
+            vreg[i] = u32x4{0, 0, 0, 0};
+            if (gk < kend) {
+                const int64_t blk = bt[gk >> log2_bs];
+                if (blk >= 0 && blk < num_blocks)
+                    vreg[i] = value_cache[(((blk * num_kv_heads + kvh) << log2_bs) + (gk & bs_mask)) * CH + vdg];
+            }
+        }
+    };
+    auto store_tile = [&]() {
 #pragma unroll
-            for (int db = 0; db < 8; ++db) orow[db * 16 + lr] = (uint16_t)f32_to_bf16_rne(o[rb][db][i] * inv);
+        for (int c = 0; c < 4; ++c) {
+            const int idx = tid + c * PF_THREADS;
+            *(u32x4 *)&sK[(idx / CH) * PF_KPAD + (idx % CH) * 8] = kreg[c];
+        }
+        // V^T: dim 8*vdg + 2j (+1) gets keys 4*vkg..+4 as two bf16 pairs
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x2 lo = u32x2{pair_lo(vreg[0][j], vreg[1][j]), pair_lo(vreg[2][j], vreg[3][j])};
+            const u32x2 hi = u32x2{pair_hi(vreg[0][j], vreg[1][j]), pair_hi(vreg[2][j], vreg[3][j])};
+            *(u32x2 *)&sV[(vdg * 8 + 2 * j) * PF_VPAD + vkg * 4] = lo;
+            *(u32x2 *)&sV[(vdg * 8 + 2 * j + 1) * PF_VPAD + vkg * 4] = hi;
+        }
+    };
+
+    f32x4 o[8][2];                            // O^T blocks: dims 16*db + 4*lb + i, row 16*qb + lr
+    float m[2], l[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[qb] = PF_M_INIT;
+        l[qb] = 0.f;
+    }
+
+    load_tile(0);
+    store_tile();
+    __syncthreads();
+    for (int kt = 0; kt < ntiles; ++kt) {
+        const int key0 = kt * PF_BN;
+        if (kt + 1 < ntiles) load_tile(key0 + PF_BN);      // in flight during this tile's math
+
+        // S^T = K Q^T: s[kb][qb] holds keys 16*kb + 4*lb + i of row 16*qb + lr
+        f32x4 s[4][2];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            s[kb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+            s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const u32x4 ka = *(const u32x4 *)&sK[(kb * 16 + lr) * PF_KPAD + lb * 8 + ks * 32];
+                s[kb][0] = mfma16x16x32(ka, qb_reg[0][ks], s[kb][0]);
+                s[kb][1] = mfma16x16x32(ka, qb_reg[1][ks], s[kb][1]);
+            }
+        }
+
+        // mask, online softmax per row, rounded weights packed as the B operand of O^T += V^T P^T
+        // (scores stay unscaled until the exponent: scale > 0 keeps the max; m is kept in scaled units)
+        const bool masked = key0 + PF_BN > kfull;            // some key of this tile is hidden from a row
+        if (masked) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = key0 + kb * 16 + lb * 4 + i;
+                        if (!(row_ok[qb] && key <= kmax[qb])) s[kb][qb][i] = -INFINITY;
+                    }
+        }
+        float m_new[2];
+        bool grow = false;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                mx = fmaxf(fmaxf(mx, fmaxf(s[kb][qb][0], s[kb][qb][1])), fmaxf(s[kb][qb][2], s[kb][qb][3]));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            m_new[qb] = fmaxf(m[qb], mx * scale_log2e);
+            grow |= m_new[qb] > m[qb];
+        }
+        if (__builtin_amdgcn_ballot_w64(grow)) {             // rescale only when a running max grew
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const float alpha = fast_exp2(m[qb] - m_new[qb]);
+                l[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < 8; ++db) o[db][qb] *= alpha;
+                m[qb] = m_new[qb];
+            }
+        }
+        u32x4 pb[2][2];                                      // [ks][qb]
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const float nm = -m[qb];
+            float rs = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                uint32_t w[4];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int kb = 2 * ks + half;
+                    w[2 * half] = pack_bf16x2(fast_exp2(fmaf(s[kb][qb][0], scale_log2e, nm)),
+                                              fast_exp2(fmaf(s[kb][qb][1], scale_log2e, nm)));
+                    w[2 * half + 1] = pack_bf16x2(fast_exp2(fmaf(s[kb][qb][2], scale_log2e, nm)),
+                                                  fast_exp2(fmaf(s[kb][qb][3], scale_log2e, nm)));
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rs = dot2_bf16(w[e], 0x3f803f80u, rs);   // sum of the rounded weights
+                pb[ks][qb] = u32x4{w[0], w[1], w[2], w[3]};
+            }
+            l[qb] += rs;
+        }
+
+        // O^T += V^T P^T: A operand = V^T rows (dims) with keys {4b..4b+3} and {16+4b..16+4b+3} of the step
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                const uint16_t *vrow = &sV[(db * 16 + lr) * PF_VPAD + ks * 32 + lb * 4];
+                const u32x2 a0 = *(const u32x2 *)vrow;
+                const u32x2 a1 = *(const u32x2 *)(vrow + 16);
+                const u32x4 va = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                o[db][0] = mfma16x16x32(va, pb[ks][0], o[db][0]);
+                o[db][1] = mfma16x16x32(va, pb[ks][1], o[db][1]);
+            }
+        }
+        __syncthreads();                                     // every wave is done with this tile
+        if (kt + 1 < ntiles) {
+            store_tile();
+            __syncthreads();
+        }
+    }
+
+    // normalise and write: lane holds dims 16*db + 4*lb + i of row 16*qb + lr
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        float lsum = l[qb];
+        lsum += __shfl_xor(lsum, 16);
+        lsum += __shfl_xor(lsum, 32);
+        const int r = wave * PF_WROWS + qb * 16 + lr;
+        const int pos = r / G, h = r % G;
+        if (!row_ok[qb]) continue;
+        const float inv = 1.0f / lsum;
+        uint16_t *orow = out + ((int64_t)(q0 + pos0 + pos) * num_heads + kvh * G + h) * PF_D;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const u32x2 pk = u32x2{pack_bf16x2(o[db][qb][0] * inv, o[db][qb][1] * inv),
+                                   pack_bf16x2(o[db][qb][2] * inv, o[db][qb][3] * inv)};
+            *(u32x2 *)&orow[db * 16 + lb * 4] = pk;
         }
     }
 }
@@ -228,11 +299,13 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
 template <int G>
 static hipError_t launch_prefill_g(const PrefillArgs &a, hipStream_t stream) {
     constexpr int BQ = PF_ROWS / G;
-    dim3 grid((a.max_seqlen_q + BQ - 1) / BQ, a.num_kv_heads, a.num_seqs);
-    hipLaunchKernelGGL((prefill_kernel<G>), grid, dim3(PF_THREADS), 0, stream, (uint16_t *)a.out,
+    const int num_q_tiles = (a.max_seqlen_q + BQ - 1) / BQ;
+    const int64_t groups = (int64_t)a.num_seqs * a.num_kv_heads;
+    const int64_t wgs = (groups + PF_XCDS - 1) / PF_XCDS * PF_XCDS * num_q_tiles;
+    hipLaunchKernelGGL((prefill_kernel<G>), dim3((unsigned)wgs), dim3(PF_THREADS), 0, stream, (uint16_t *)a.out,
                        (const u32x4 *)a.query, (const u32x4 *)a.key_cache, (const u32x4 *)a.value_cache, a.block_tables,
-                       a.bt_stride, a.cu_seqlens_q, a.cu_seqlens_k, a.max_seqlen_k, a.num_kv_heads, a.num_blocks,
-                       a.log2_bs, a.scale_log2e, a.causal);
+                       a.bt_stride, a.cu_seqlens_q, a.cu_seqlens_k, a.num_seqs, a.max_seqlen_k, num_q_tiles,
+                       a.num_kv_heads, a.num_blocks, a.log2_bs, a.scale_log2e, a.causal);
     return hipGetLastError();
 }
 
