@@ -48,6 +48,24 @@ def store_bytes(c) -> int:
     return int(n * c.num_kv_heads * c.head_dim * e * 2 * 2 + 4 * n)
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per decode call from the committed rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, each
+    scaled by the same counter on a copy of known size), or None when the counters were taken on other
+    kernel sources than the ones built now, or on another workload."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as f:
+        doc = json.load(f)
+    h = hashlib.sha256()
+    for src in doc["kernel_sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return doc["decode_call_traffic_bytes"] if h.hexdigest() == doc["kernel_sources_sha256"] else None
+
+
 def cpu_baseline(c, target_s=12.0):
     """Time the oracle (float64, all host cores) on a bounded sample of the same workload: the decode of
     the whole batch, repeated until about target_s seconds of CPU work (fewer sequences if one pass is
@@ -252,7 +270,7 @@ def main():
         "step_bytes": step_bytes,
         "roofline": {"bound": "hbm", "kernel": "paged_attention_decode call (decode_kernel + decode_reduce_kernel)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(c.name),
                      "avg_launch_ms": round(dec_avg_ms, 5), "algorithmic_bytes": decode_bytes(c)},
         "outputs_finite": finite,
         "gpu": torch.cuda.get_device_name(0),

@@ -19,6 +19,11 @@ HIPCC_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
                "-I", CSRC, "-I", INCLUDE]
 
 
+# prefill: softmax maxima over MFMA results need no NaN quieting (masked scores are -inf, never NaN),
+# so IEEE mode is off there and fmax is a single v_max_f32.
+FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+
+
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     return os.path.join(rocm, "bin", "hipcc")
@@ -31,7 +36,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     def compile_one(src):
         obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
-        cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
