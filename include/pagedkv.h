@@ -60,7 +60,8 @@ typedef enum {
     PKV_EINVAL = 1,
     PKV_EUNSUPPORTED = 2,
     PKV_EWORKSPACE = 3,
-    PKV_EHIP = 4
+    PKV_EHIP = 4,
+    PKV_ENOMEM = 5          /* host block manager: too few free blocks */
 } pkv_status;
 
 /*
@@ -78,9 +79,10 @@ pkv_status pkv_kv_cache_store(pkv_dtype dtype, const void *key, const void *valu
                               hipStream_t stream);
 
 /*
- * Bytes of device workspace pkv_paged_attention_decode needs for these sizes (0: none). Long
- * contexts are split into partitions whose partial softmax state (fp32 max, sum and head_dim
- * accumulators per sequence, head and partition) is merged by a reduce pass.
+ * Bytes of device workspace pkv_paged_attention_decode needs for these sizes (0 only when num_seqs is
+ * 0): a work list of 16 bytes per (sequence, partition) plus, when max_context_len spans several
+ * partitions, the partial softmax state (fp32 max, sum and head_dim accumulators per sequence, head
+ * and partition) merged by a reduce pass.
  */
 size_t pkv_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                                  int32_t head_dim, int32_t block_size, int32_t max_context_len);
@@ -89,14 +91,18 @@ size_t pkv_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_h
  * paged_attention_decode. For sequence i and query head h (kv head h / G, G = num_heads / num_kv_heads):
  *   out[i][h] = sum_{t < context_lens[i]} softmax_t(scale * query[i][h] . K_i[t]) V_i[t],
  * with K_i[t] = key_cache[block_tables[i][t / block_size]][h / G][t % block_size] and likewise V.
- * A sequence with context_lens[i] == 0 gets zeros. fp32 data accumulates in fp32; bf16 data
- * accumulates in fp32 and rounds the output to bf16 (nearest even).
+ * A sequence with context_lens[i] == 0 gets zeros. fp32 data computes in fp32. bf16 data: q.k and
+ * p.v run on v_dot2_f32_bf16 with fp32 accumulation, the softmax weights of two tokens rounded to a
+ * bf16 pair for p.v (their sum, the denominator, uses the same rounded weights); output rounded to
+ * bf16 (nearest even).
  * Source: "推理运行时", section 分页 KV (attention reads K/V through the block table);
  * "LLM Infra 101 v0.2: KV Cache", section 推理 (decode attends to the cache plus the new token).
  * block_tables: device int32 [num_seqs][block_table_stride]; context_lens: device int32 [num_seqs];
  * max_context_len: host bound on context_lens (sizes the grid and the workspace), must be
- * <= block_table_stride * block_size. workspace: device memory of at least
- * pkv_paged_attention_decode_workspace_size(...) bytes (may be NULL when that is 0).
+ * <= block_table_stride * block_size. workspace: device memory, 256-byte aligned, of at least
+ * pkv_paged_attention_decode_workspace_size(...) bytes; it holds the work list the call builds on the
+ * device (longest partitions first) and the split-K partials. A call overwrites it; calls that share a
+ * workspace must be ordered on one stream.
  * head_dim in {64, 128}; num_heads / num_kv_heads in 1..8.
  */
 pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *query, const void *key_cache,
@@ -140,6 +146,17 @@ pkv_status pkv_kv_cache_gather(pkv_dtype dtype, void *key_out, void *value_out, 
                                const void *value_cache, const int32_t *block_table_row, int32_t len,
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                                hipStream_t stream);
+
+/*
+ * kv_cache_copy_blocks: for each pair k, physical block pairs[2k+1] of both caches becomes a copy of
+ * block pairs[2k] (all kv heads, all block_size rows). Used for copy-on-write of a shared block before a
+ * branch writes into it ("推理运行时", section Prefix cache 与 copy-on-write). pairs: device int32
+ * [2 * num_pairs]; destinations must be distinct and no destination may be a source of another pair;
+ * ids outside [0, num_blocks) are skipped.
+ */
+pkv_status pkv_kv_cache_copy_blocks(pkv_dtype dtype, void *key_cache, void *value_cache, const int32_t *pairs,
+                                    int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int64_t num_blocks, hipStream_t stream);
 
 /* Message of the calling thread's last non-OK status ("" if none). Owned by the library. */
 const char *pkv_last_error(void);

@@ -60,6 +60,8 @@ class Oracle:
         P, I32, I64, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         lib.orc_store.argtypes = [ctypes.c_int, P, P, P, P, P, I64, I32, I32, I32, I64]
         lib.orc_gather.argtypes = [ctypes.c_int, P, P, P, P, P, I32, I32, I32, I32, I64]
+        lib.orc_copy_blocks.argtypes = [ctypes.c_int, P, P, P, I32, I32, I32, I32, I64]
+        lib.orc_copy_blocks.restype = ctypes.c_int
         lib.orc_decode.argtypes = [ctypes.c_int, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I64, D,
                                    P, I32, I32]
         lib.orc_prefill.argtypes = [ctypes.c_int, P, P, P, P, P, I32, P, P, I32, I32, I32, I32, I32, I64, D,
@@ -92,6 +94,17 @@ class Oracle:
         nb, hkv, bs, d = key_cache.shape
         self._check(self.lib.orc_store(_DT[dtype], _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
                                        _ptr(sm), len(sm), hkv, d, bs, nb))
+
+    def copy_blocks(self, dtype, key_cache, value_cache, pairs):
+        """In place: block pairs[k, 1] of both caches becomes a copy of block pairs[k, 0]."""
+        sd = _store_dtype(dtype)
+        for a in (key_cache, value_cache):
+            if a.dtype != sd or not a.flags.c_contiguous:
+                raise TypeError("caches must be C-contiguous arrays of the storage dtype")
+        pr = _c(pairs, np.int32).reshape(-1, 2)
+        nb, hkv, bs, d = key_cache.shape
+        self._check(self.lib.orc_copy_blocks(_DT[dtype], _ptr(key_cache), _ptr(value_cache), _ptr(pr), len(pr), hkv, d,
+                                             bs, nb))
 
     def gather(self, dtype, key_cache, value_cache, block_table_row, length):
         """Logical tokens ``[0, length)`` of one block table as contiguous ``[length, Hkv, D]`` K and V."""
@@ -169,6 +182,10 @@ def store(*a, **k):
 
 def gather(*a, **k):
     return default().gather(*a, **k)
+
+
+def copy_blocks(*a, **k):
+    return default().copy_blocks(*a, **k)
 
 
 def decode(*a, **k):

@@ -98,6 +98,27 @@ int orc_store(int dtype, const void *key, const void *value, void *key_cache, vo
     return ORC_OK;
 }
 
+/* Copy blocks: for each pair k, physical block pairs[2k+1] of both caches becomes a copy of block pairs[2k]
+ * (copy-on-write of a shared block). Sources are read before any destination is written. */
+int orc_copy_blocks(int dtype, void *key_cache, void *value_cache, const int32_t *pairs, int32_t num_pairs,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks) {
+    size_t block_bytes = (size_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype);
+    for (int32_t k = 0; k < 2 * num_pairs; ++k)
+        if (pairs[k] < 0 || pairs[k] >= num_blocks) return fail("block id %d outside the pool of %lld", pairs[k], (long long)num_blocks);
+    char *tmp = (char *)malloc(block_bytes * 2 * (size_t)(num_pairs > 0 ? num_pairs : 1));
+    if (!tmp) return fail("out of memory");
+    for (int32_t k = 0; k < num_pairs; ++k) {
+        memcpy(tmp + (2 * (size_t)k) * block_bytes, (char *)key_cache + (size_t)pairs[2 * k] * block_bytes, block_bytes);
+        memcpy(tmp + (2 * (size_t)k + 1) * block_bytes, (char *)value_cache + (size_t)pairs[2 * k] * block_bytes, block_bytes);
+    }
+    for (int32_t k = 0; k < num_pairs; ++k) {
+        memcpy((char *)key_cache + (size_t)pairs[2 * k + 1] * block_bytes, tmp + (2 * (size_t)k) * block_bytes, block_bytes);
+        memcpy((char *)value_cache + (size_t)pairs[2 * k + 1] * block_bytes, tmp + (2 * (size_t)k + 1) * block_bytes, block_bytes);
+    }
+    free(tmp);
+    return ORC_OK;
+}
+
 /* Gather: logical tokens [0, len) of one block table into contiguous rows [len][num_kv_heads][head_dim]. */
 int orc_gather(int dtype, void *key_out, void *value_out, const void *key_cache, const void *value_cache,
                const int32_t *block_table_row, int32_t len, int32_t num_kv_heads, int32_t head_dim,

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 
 PKV_F32, PKV_BF16 = 0, 1
-STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP"}
+STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP", 5: "PKV_ENOMEM"}
 
 _lib = None
 
@@ -52,12 +52,39 @@ def load_library(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    lib.pkv_kv_cache_copy_blocks.argtypes = [ctypes.c_int, P, P, P, I32, I32, I32, I32, I64, P]
+    lib.pkv_kv_cache_copy_blocks.restype = ctypes.c_int
+    H = ctypes.c_void_p
+    lib.pkv_bm_create.argtypes = [I32, I32, I32, ctypes.POINTER(H)]
+    lib.pkv_bm_destroy.argtypes = [H]
+    lib.pkv_bm_destroy.restype = None
+    lib.pkv_bm_allocate.argtypes = [H, I64, I32, P, ctypes.POINTER(I32)]
+    lib.pkv_bm_append.argtypes = [H, I64, I32, P]
+    lib.pkv_bm_fork.argtypes = [H, I64, I64]
+    lib.pkv_bm_release.argtypes = [H, I64]
+    lib.pkv_bm_block_table.argtypes = [H, I64, P, I32, ctypes.POINTER(I32), ctypes.POINTER(I64)]
+    lib.pkv_bm_slot_mapping.argtypes = [H, I64, I64, I32, P]
+    lib.pkv_bm_take_copies.argtypes = [H, P, I32, ctypes.POINTER(I32)]
+    lib.pkv_bm_usage.argtypes = [H, ctypes.POINTER(BlockUsage)]
+    for name in ("pkv_bm_create", "pkv_bm_allocate", "pkv_bm_append", "pkv_bm_fork", "pkv_bm_release",
+                 "pkv_bm_block_table", "pkv_bm_slot_mapping", "pkv_bm_take_copies", "pkv_bm_usage"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.pkv_bm_last_error.restype = ctypes.c_char_p
     lib.pkv_paged_attention_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.pkv_paged_attention_decode_workspace_size.restype = SZ
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_version.restype = ctypes.c_char_p
     _lib = lib
     return lib
+
+
+class BlockUsage(ctypes.Structure):
+    _fields_ = [("num_requests", ctypes.c_int64), ("allocated_tokens", ctypes.c_int64),
+                ("reserved_tokens", ctypes.c_int64), ("internal_fragmentation_tokens", ctypes.c_int64),
+                ("block_utilization", ctypes.c_double), ("used_blocks", ctypes.c_int64),
+                ("free_blocks", ctypes.c_int64), ("max_request_tokens", ctypes.c_int64),
+                ("contiguous_reserved_tokens", ctypes.c_int64), ("contiguous_fragmentation_tokens", ctypes.c_int64),
+                ("contiguous_utilization", ctypes.c_double)]
 
 
 def _check(rc: int):
@@ -181,3 +208,121 @@ def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, cu
                                            _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), b, int(max_seqlen_q),
                                            int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), int(bool(causal)),
                                            _stream(stream)))
+
+
+def kv_cache_copy_blocks(key_cache, value_cache, pairs, stream=None):
+    """Copy whole physical blocks of both caches: ``pairs`` is a device int32 tensor [n, 2] of (src, dst)."""
+    lib = load_library()
+    _dev(key_cache, value_cache, pairs)
+    _i32(pairs)
+    nb, hkv, bs, d = key_cache.shape
+    if value_cache.shape != key_cache.shape or key_cache.dtype != value_cache.dtype:
+        raise ValueError("both caches must be [NB, Hkv, bs, D] of one dtype")
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n, 2]")
+    _check(lib.pkv_kv_cache_copy_blocks(_dtype_code(key_cache), _ptr(key_cache), _ptr(value_cache), _ptr(pairs),
+                                        pairs.shape[0], hkv, d, bs, nb, _stream(stream)))
+
+
+class BlockManager:
+    """Host KV block manager (the C++ one in libpagedkv.so): per-request block tables over a pool of
+    ``total_blocks`` blocks of ``block_size`` tokens, with optional prefix caching and copy-on-write."""
+
+    def __init__(self, total_blocks: int, block_size: int = 16, prefix_caching: bool = False):
+        self._lib = load_library()
+        h = ctypes.c_void_p()
+        self._bm_check(self._lib.pkv_bm_create(total_blocks, block_size, int(prefix_caching), ctypes.byref(h)))
+        self._h = h
+        self.total_blocks, self.block_size, self.prefix_caching = total_blocks, block_size, prefix_caching
+
+    def _bm_check(self, rc):
+        if rc != 0:
+            raise PagedKVError(rc, self._lib.pkv_bm_last_error().decode())
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pkv_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    @staticmethod
+    def _tok(token_ids):
+        import numpy as np
+
+        return None if token_ids is None else np.ascontiguousarray(token_ids, dtype=np.int32)
+
+    def allocate(self, request_id: int, num_tokens: int, token_ids=None) -> int:
+        """Blocks for a new request; returns the number of prompt tokens served from cached blocks."""
+        tok = self._tok(token_ids)
+        cached = ctypes.c_int32(0)
+        self._bm_check(self._lib.pkv_bm_allocate(self._h, request_id, num_tokens,
+                                                 None if tok is None else tok.ctypes.data_as(ctypes.c_void_p),
+                                                 ctypes.byref(cached)))
+        return cached.value
+
+    def append(self, request_id: int, num_tokens: int = 1, token_ids=None):
+        tok = self._tok(token_ids)
+        self._bm_check(self._lib.pkv_bm_append(self._h, request_id, num_tokens,
+                                               None if tok is None else tok.ctypes.data_as(ctypes.c_void_p)))
+
+    def fork(self, parent_id: int, child_id: int):
+        self._bm_check(self._lib.pkv_bm_fork(self._h, parent_id, child_id))
+
+    def release(self, request_id: int):
+        self._bm_check(self._lib.pkv_bm_release(self._h, request_id))
+
+    def block_table(self, request_id: int):
+        import numpy as np
+
+        nb, nt = ctypes.c_int32(0), ctypes.c_int64(0)
+        self._bm_check(self._lib.pkv_bm_block_table(self._h, request_id, None, 0, ctypes.byref(nb), ctypes.byref(nt)))
+        out = np.empty(nb.value, dtype=np.int32)
+        self._bm_check(self._lib.pkv_bm_block_table(self._h, request_id, out.ctypes.data_as(ctypes.c_void_p),
+                                                    nb.value, ctypes.byref(nb), ctypes.byref(nt)))
+        return out
+
+    def num_tokens(self, request_id: int) -> int:
+        nb, nt = ctypes.c_int32(0), ctypes.c_int64(0)
+        self._bm_check(self._lib.pkv_bm_block_table(self._h, request_id, None, 0, ctypes.byref(nb), ctypes.byref(nt)))
+        return nt.value
+
+    def slot_mapping(self, request_id: int, first_position: int, count: int):
+        import numpy as np
+
+        out = np.empty(count, dtype=np.int32)
+        self._bm_check(self._lib.pkv_bm_slot_mapping(self._h, request_id, first_position, count,
+                                                     out.ctypes.data_as(ctypes.c_void_p)))
+        return out
+
+    def take_copies(self):
+        """Pending copy-on-write pairs as an int32 array [n, 2] of (src, dst); empties the queue."""
+        import numpy as np
+
+        n = ctypes.c_int32(0)
+        self._bm_check(self._lib.pkv_bm_take_copies(self._h, None, 0, ctypes.byref(n)))
+        out = np.empty((n.value, 2), dtype=np.int32)
+        if n.value:
+            self._bm_check(self._lib.pkv_bm_take_copies(self._h, out.ctypes.data_as(ctypes.c_void_p), n.value,
+                                                        ctypes.byref(n)))
+        return out
+
+    def usage(self) -> dict:
+        u = BlockUsage()
+        self._bm_check(self._lib.pkv_bm_usage(self._h, ctypes.byref(u)))
+        return {name: getattr(u, name) for name, _ in BlockUsage._fields_}
+
+    def build_tables(self, request_ids, stride: int | None = None):
+        """Block tables [n, stride] (padded with -1; stride defaults to the longest table rounded up to a
+        multiple of 32 entries) and the requests' token counts, as int32 numpy arrays."""
+        import numpy as np
+
+        tables = [self.block_table(r) for r in request_ids]
+        lens = np.array([self.num_tokens(r) for r in request_ids], dtype=np.int32)
+        longest = max((len(t) for t in tables), default=0)
+        stride = stride or max(32, (longest + 31) // 32 * 32)
+        out = np.full((len(tables), stride), -1, dtype=np.int32)
+        for i, t in enumerate(tables):
+            out[i, :len(t)] = t
+        return out, lens

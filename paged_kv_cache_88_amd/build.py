@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libpagedkv.so")
-SOURCES = ["api.hip", "store.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "store.hip", "decode.hip", "prefill.hip", "block_manager.cpp"]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are disabled for the device code: hipcc would otherwise form them from
@@ -35,7 +35,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(obj_dir, exist_ok=True)
 
     def compile_one(src):
-        obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
         cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:

@@ -151,6 +151,21 @@ pkv_status pkv_kv_cache_gather(pkv_dtype dtype, void *key_out, void *value_out, 
                       "kv_cache_gather launch");
 }
 
+pkv_status pkv_kv_cache_copy_blocks(pkv_dtype dtype, void *key_cache, void *value_cache, const int32_t *pairs,
+                                    int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int64_t num_blocks, hipStream_t stream) {
+    pkv_status st = check_common(dtype, num_kv_heads, head_dim, block_size, num_blocks);
+    if (st != PKV_OK) return st;
+    REQUIRE(num_pairs >= 0 && num_pairs <= 65535, PKV_EINVAL, "num_pairs %d outside [0, 65535]", num_pairs);
+    if (num_pairs == 0) return ok();
+    REQUIRE(key_cache && value_cache && pairs, PKV_EINVAL, "null pointer argument");
+    REQUIRE(aligned16(key_cache) && aligned16(value_cache), PKV_EINVAL, "cache pointers must be 16-byte aligned");
+    const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype);
+    return hip_status(pkv::launch_copy_blocks(key_cache, value_cache, pairs, num_pairs, block_bytes, (int)num_blocks,
+                                              stream),
+                      "kv_cache_copy_blocks launch");
+}
+
 size_t pkv_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                                  int32_t head_dim, int32_t block_size, int32_t max_context_len) {
     if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || log2_exact(block_size) < 0) return 0;

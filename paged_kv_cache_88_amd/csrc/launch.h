@@ -16,6 +16,9 @@ hipError_t launch_gather(void *key_out, void *value_out, const void *key_cache, 
                          const int32_t *block_table_row, int64_t len, int num_kv_heads, int row_bytes,
                          int block_size, int num_blocks, hipStream_t stream);
 
+hipError_t launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *pairs, int num_pairs, int64_t block_bytes,
+                              int num_blocks, hipStream_t stream);
+
 struct DecodeArgs {
     void *out;
     const void *query;

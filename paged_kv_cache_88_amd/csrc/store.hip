@@ -8,6 +8,8 @@
 // Work decomposition: one thread moves 16 bytes. A (token, kv head) row is head_dim * elem
 // bytes = CHUNKS 16-byte pieces; consecutive threads take consecutive pieces of the same row, so
 // each wave reads a contiguous run of the source and writes whole 128-byte lines of the cache.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -59,6 +61,28 @@ __global__ void __launch_bounds__(256) gather_kernel(u32x4 *__restrict__ key_out
     int64_t src = cache_row(block, kvh, off, num_kv_heads, block_size) * CHUNKS + chunk;
     key_out[row * CHUNKS + chunk] = key_cache[src];
     value_out[row * CHUNKS + chunk] = value_cache[src];
+}
+
+// Copy whole blocks (all kv heads): one thread moves 16 bytes; blockIdx.y is the pair.
+__global__ void __launch_bounds__(256) copy_blocks_kernel(u32x4 *__restrict__ key_cache, u32x4 *__restrict__ value_cache,
+                                                          const int32_t *__restrict__ pairs, int64_t block_vecs,
+                                                          int num_blocks) {
+    const int32_t src = pairs[2 * blockIdx.y], dst = pairs[2 * blockIdx.y + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < block_vecs; i += (int64_t)gridDim.x * blockDim.x) {
+        key_cache[(int64_t)dst * block_vecs + i] = key_cache[(int64_t)src * block_vecs + i];
+        value_cache[(int64_t)dst * block_vecs + i] = value_cache[(int64_t)src * block_vecs + i];
+    }
+}
+
+hipError_t launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *pairs, int num_pairs, int64_t block_bytes,
+                              int num_blocks, hipStream_t stream) {
+    if (num_pairs == 0) return hipSuccess;
+    const int64_t vecs = block_bytes / 16;
+    const unsigned gx = (unsigned)std::min<int64_t>((vecs + 255) / 256, 64);
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, num_pairs), dim3(256), 0, stream, (u32x4 *)key_cache,
+                       (u32x4 *)value_cache, pairs, vecs, num_blocks);
+    return hipGetLastError();
 }
 
 hipError_t launch_store(const void *key, const void *value, void *key_cache, void *value_cache,
