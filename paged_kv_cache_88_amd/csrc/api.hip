@@ -71,19 +71,45 @@ pkv_status check_heads(int32_t num_heads, int32_t num_kv_heads) {
     return ok();
 }
 
-// Decode partitioning: partitions of DECODE_PART tokens (a multiple of every supported block size)
-// keep each workgroup's share of a long context bounded, so a batch with a long tail still spreads
-// over all compute units; sequences that fit one partition skip the reduce.
-#ifndef PKV_DECODE_PART
-#define PKV_DECODE_PART 1024
+// Decode work sizing. The plan kernel cuts sequences into parts on the device (see decode.hip); the host
+// fixes the bounds it works within:
+//   workers: resident one-wave workgroups, 8 per compute unit (2 per SIMD at the decode kernels'
+//     register budget), capped at DECODE_MAX_WORKERS (MI355X: 256 CUs); the plan aims at
+//     DECODE_UNITS_PER_WORKER units per worker, so a longest-first schedule can even out the ends;
+//   max part length: its block-table slice must fit the 64 lanes of a wave (64 blocks when parts start on
+//     a block boundary, i.e. block_size <= 32; 63 otherwise), in whole 32-token tiles;
+//   min part length: DECODE_MIN_PART_TILES tiles, so partials never dominate the traffic.
+// The number of parts is at most 2 B + ceil(target_units / Hkv) + ceil(B * ceil(max_context_len / 32) / max_tiles)
+// (each sequence adds at most one part above its share of the target length and one above its share of
+// the slice limit), which sizes the work list and the partial buffers.
+#ifndef PKV_DECODE_UNITS_PER_WORKER
+#define PKV_DECODE_UNITS_PER_WORKER 1
 #endif
-constexpr int DECODE_PART = PKV_DECODE_PART;
+#ifndef PKV_DECODE_WAVES_PER_CU
+#define PKV_DECODE_WAVES_PER_CU 8
+#endif
+constexpr int DECODE_WAVES_PER_CU = PKV_DECODE_WAVES_PER_CU;
+constexpr int DECODE_MAX_WORKERS = 256 * DECODE_WAVES_PER_CU;
+constexpr int DECODE_UNITS_PER_WORKER = PKV_DECODE_UNITS_PER_WORKER;
+constexpr int DECODE_MIN_PART_TILES = 4;
+
+int decode_workers() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return DECODE_MAX_WORKERS;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    const int w = cus * DECODE_WAVES_PER_CU < DECODE_MAX_WORKERS ? cus * DECODE_WAVES_PER_CU : DECODE_MAX_WORKERS;
+    if (dev < 64) cached[dev] = w;
+    return w;
+}
 
 struct DecodePlan {
-    int part_tokens;
-    int num_parts;
+    int max_part_tiles;
+    int64_t max_items;
     size_t ws_bytes;
-    size_t off_items, off_m, off_l, off_o;
+    size_t off_items, off_info, off_m, off_l, off_o;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -91,21 +117,21 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int32_t max_context_len) {
     DecodePlan p{};
-    // a partition spans at most decode_max_part_blocks() blocks (its table slice lives in one register)
-    p.part_tokens = DECODE_PART < block_size * pkv::decode_max_part_blocks() ? DECODE_PART
-                                                                             : block_size * pkv::decode_max_part_blocks();
-    p.num_parts = max_context_len <= 0 ? 1 : (max_context_len + p.part_tokens - 1) / p.part_tokens;
-    // [ctrl: 256 B][work items: num_seqs * num_parts int4][partials when num_parts > 1]
-    (void)num_kv_heads;
+    const int tile = pkv::decode_tile_tokens();
+    const int slice_blocks = block_size <= tile ? pkv::decode_max_part_blocks() : pkv::decode_max_part_blocks() - 1;
+    p.max_part_tiles = slice_blocks * block_size / tile;
+    const int64_t max_tiles_per_seq = ((int64_t)(max_context_len > 0 ? max_context_len : 0) + tile - 1) / tile;
+    p.max_items = 2 * (int64_t)num_seqs +
+                  ((int64_t)DECODE_MAX_WORKERS * DECODE_UNITS_PER_WORKER + num_kv_heads - 1) / num_kv_heads +
+                  ((int64_t)num_seqs * max_tiles_per_seq + p.max_part_tiles - 1) / p.max_part_tiles;
+    // [ctrl: 256 B][work list][per-sequence info][partials m, l, o]
+    const size_t n = (size_t)p.max_items * num_heads;
     p.off_items = 256;
-    p.ws_bytes = p.off_items + align256((size_t)num_seqs * p.num_parts * 16);
-    if (p.num_parts > 1) {
-        size_t n = (size_t)num_seqs * num_heads * p.num_parts;
-        p.off_m = p.ws_bytes;
-        p.off_l = p.off_m + align256(n * sizeof(float));
-        p.off_o = p.off_l + align256(n * sizeof(float));
-        p.ws_bytes = p.off_o + n * head_dim * sizeof(float);
-    }
+    p.off_info = p.off_items + align256((size_t)p.max_items * 16);
+    p.off_m = p.off_info + align256((size_t)num_seqs * 16);
+    p.off_l = p.off_m + align256(n * sizeof(float));
+    p.off_o = p.off_l + align256(n * sizeof(float));
+    p.ws_bytes = p.off_o + n * head_dim * sizeof(float);
     return p;
 }
 
@@ -196,12 +222,10 @@ pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *qu
     REQUIRE(aligned16(out) && aligned16(query) && aligned16(key_cache) && aligned16(value_cache), PKV_EINVAL,
             "out, query and cache pointers must be 16-byte aligned");
     DecodePlan plan = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len);
-    REQUIRE(plan.part_tokens / block_size <= pkv::decode_max_part_blocks(), PKV_EUNSUPPORTED,
-            "partition spans too many blocks");
-    REQUIRE(plan.num_parts <= 32767, PKV_EINVAL, "max_context_len too large (at most 32767 partitions of %d tokens)",
-            plan.part_tokens);
-    REQUIRE((int64_t)num_seqs * plan.num_parts * num_kv_heads <= (int64_t)1 << 24, PKV_EINVAL,
-            "decode grid too large (num_seqs * partitions * num_kv_heads above 2^24)");
+    REQUIRE((int64_t)num_seqs * (((int64_t)max_context_len + 31) / 32) < ((int64_t)1 << 30), PKV_EINVAL,
+            "num_seqs * max_context_len too large (at most 2^35 tokens)");
+    REQUIRE(plan.max_items * num_kv_heads <= (int64_t)1 << 26, PKV_EINVAL,
+            "decode work list too large (num_kv_heads * parts above 2^26)");
     REQUIRE(workspace != nullptr && workspace_bytes >= plan.ws_bytes, PKV_EWORKSPACE,
             "decode needs %zu bytes of workspace (got %zu)", plan.ws_bytes, workspace_bytes);
     REQUIRE(((uintptr_t)workspace & 255u) == 0, PKV_EINVAL, "workspace must be 256-byte aligned");
@@ -218,16 +242,18 @@ pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *qu
     a.num_kv_heads = num_kv_heads;
     a.num_blocks = num_blocks;
     a.log2_bs = log2_exact(block_size);
-    a.part_tokens = plan.part_tokens;
-    a.num_parts = plan.num_parts;
+    a.workers = decode_workers();
+    a.target_units = a.workers * DECODE_UNITS_PER_WORKER;
+    a.max_part_tiles = plan.max_part_tiles;
+    a.min_part_tiles = DECODE_MIN_PART_TILES;
+    a.max_items = plan.max_items;
     a.scale_log2e = scale * 1.4426950408889634f;
     a.ctrl = (int *)workspace;
     a.items = (int4 *)((char *)workspace + plan.off_items);
-    if (plan.num_parts > 1) {
-        a.ws_m = (float *)((char *)workspace + plan.off_m);
-        a.ws_l = (float *)((char *)workspace + plan.off_l);
-        a.ws_o = (float *)((char *)workspace + plan.off_o);
-    }
+    a.seq_info = (int4 *)((char *)workspace + plan.off_info);
+    a.ws_m = (float *)((char *)workspace + plan.off_m);
+    a.ws_l = (float *)((char *)workspace + plan.off_l);
+    a.ws_o = (float *)((char *)workspace + plan.off_o);
     return hip_status(pkv::launch_decode(a, dtype == PKV_BF16, head_dim, num_heads / num_kv_heads, stream),
                       "paged_attention_decode launch");
 }

@@ -10,15 +10,14 @@
 // (Mini-SGLang 源码解析（二）, section 8.3), so the kernel is built around streaming K/V once,
 // with enough bytes in flight to cover HBM latency.
 //
-// Work decomposition. A partition is a run of part_tokens logical tokens of one sequence (a multiple
-// of block_size, spanning at most 64 blocks). A one-workgroup plan kernel reads context_lens on the
-// device and writes the list of (sequence, partition) work items sorted longest first (a counting sort
-// on the partition's token count), so long partitions are dispatched first and the batch does not end
-// on a straggler. The decode grid is one workgroup per (work item, kv head) in that order; slots past
-// the item count exit at once. A workgroup of NW waves serves all G query heads of its kv head, so
-// every K/V byte is read once. If a sequence fits one partition the workgroup writes the final output;
-// otherwise it writes an unnormalised partial (running max m, sum l, accumulator o, fp32) and the
-// reduce kernel merges the partitions with the log-sum-exp rule.
+// Work decomposition. A part is a run of tokens of one sequence; a unit is a part x one kv head, and
+// one wave serves all G query heads of its kv head, so every K/V byte is read once. A one-workgroup
+// plan kernel reads context_lens on the device and cuts every sequence into parts whose length is
+// chosen from the actual lengths of the batch, so that the batch becomes about as many units of
+// equal size as the GPU holds resident waves (long sequences are split, short ones stay whole); it
+// lists the parts longest first (a counting sort on the length). A sequence of one part writes its
+// output directly; otherwise each part writes an unnormalised partial (running max m, sum l,
+// accumulator o, fp32) and the reduce kernel merges them with the log-sum-exp rule.
 //
 // Inside a wave: LPT lanes share one token row (head_dim elements); each lane holds NV 16-byte
 // vectors of the row, so one load instruction covers RPW = 64 / LPT rows. A wave tile is R such
@@ -67,26 +66,145 @@ struct TileRegs {
 };
 
 constexpr int PLAN_THREADS = 1024;
+constexpr int PLAN_WAVES = PLAN_THREADS / 64;
 constexpr int PLAN_BUCKETS = 64;
+constexpr int DECODE_TILE = 32;               // part lengths are multiples of this many tokens
 
-// Work list for the decode grid. items[k] = {seq, part, ntok, nparts}, sorted by ntok descending in
-// PLAN_BUCKETS buckets (order inside a bucket is arbitrary: every item writes its own output, so the
-// result does not depend on it). ctrl[0] = number of items. Sequences with an empty context get zero
-// outputs here. Single workgroup.
+// Exclusive prefix sum of v over the plan workgroup; *total gets the sum. Every thread must call it.
+__device__ int plan_exclusive_scan(int v, int *s_wave, int *total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) s_wave[wave] = x;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < PLAN_WAVES; ++w) {
+        const int sw = s_wave[w];
+        before += w < wave ? sw : 0;
+        all += sw;
+    }
+    __syncthreads();                              // s_wave is reused by the next call
+    *total = all;
+    return before + x - v;
+}
+
+// Work list. Sequence i (L_i tokens, context_lens clamped to [0, max_context_len]) is cut into n_i
+// parts of len_i tokens, the last part taking the rest, where, in tiles of 32 tokens,
+//   target = max(min_tiles, ceil(num_kv_heads * sum_i ceil(L_i / 32) / target_units)),
+//   n_i    = max(1, round(tiles_i / target), ceil(tiles_i / max_tiles)),  len_i = 32 * ceil(tiles_i / n_i),
+// so the batch is about target_units units of equal size and no part spans more blocks than a lane
+// register holds. items[k] = {seq, first token, tokens, partial slot (-1 when the sequence is one
+// part)}, longest first (64-bucket counting sort; order inside a bucket is arbitrary and every unit
+// writes its own output, so results do not depend on it). seq_info[i] = {first partial slot, n_i,
+// len_i, L_i}; ctrl[0] = number of parts. Sequences with L_i = 0 get zero outputs here. One workgroup; thread t owns sequences t + k * PLAN_THREADS,
+// and keeps the first PLAN_REG of them in registers (larger batches re-read seq_info).
+constexpr int PLAN_REG = 4;
+
 __global__ void __launch_bounds__(PLAN_THREADS)
-decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int max_context_len, int part_tokens,
-                   int4 *__restrict__ items, int *__restrict__ ctrl, void *__restrict__ out, int out_row_elems,
-                   int elem_bytes) {
+decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int max_context_len, int num_kv_heads,
+                   int target_units, int max_tiles, int min_tiles, int4 *__restrict__ items, int4 *__restrict__ seq_info,
+                   int *__restrict__ ctrl, void *__restrict__ out, int out_row_elems, int elem_bytes) {
+    __shared__ int s_wave[PLAN_WAVES];
     __shared__ int hist[PLAN_BUCKETS];
     __shared__ int offs[PLAN_BUCKETS];
+    __shared__ int s_tiles, s_maxlen;
     const int tid = threadIdx.x;
     if (tid < PLAN_BUCKETS) hist[tid] = 0;
-    __syncthreads();
-    auto bucket = [&](int ntok) { return (int)(((int64_t)(part_tokens - ntok) * PLAN_BUCKETS) / part_tokens); };
-    for (int i = tid; i < num_seqs; i += PLAN_THREADS) {
-        const int L = min(context_lens[i], max_context_len);
-        for (int start = 0; start < L; start += part_tokens) atomicAdd(&hist[bucket(min(part_tokens, L - start))], 1);
+    if (tid == 0) {
+        s_tiles = 0;
+        s_maxlen = 1;
     }
+    auto clen = [&](int i) { return max(0, min(context_lens[i], max_context_len)); };
+    auto wave_sum = [](int v) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+        return v;
+    };
+    auto wave_max = [](int v) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
+        return v;
+    };
+    const bool wave_lead = (tid & 63) == 0;
+    int lreg[PLAN_REG];
+    int t = 0;
+#pragma unroll
+    for (int k = 0; k < PLAN_REG; ++k) {
+        const int i = tid + k * PLAN_THREADS;
+        lreg[k] = i < num_seqs ? clen(i) : 0;
+        t += (lreg[k] + DECODE_TILE - 1) / DECODE_TILE;
+    }
+    for (int i = tid + PLAN_REG * PLAN_THREADS; i < num_seqs; i += PLAN_THREADS)
+        t += (clen(i) + DECODE_TILE - 1) / DECODE_TILE;
+    t = wave_sum(t);
+    __syncthreads();                                  // s_tiles, hist initialised
+    if (wave_lead) atomicAdd(&s_tiles, t);
+    __syncthreads();
+    const int target = max(min_tiles, (int)(((int64_t)s_tiles * num_kv_heads + target_units - 1) / target_units));
+
+    // parts per sequence and their partial slots (exclusive scan, PLAN_THREADS sequences at a time)
+    int4 sreg[PLAN_REG];
+    int carry = 0, my_max = 1;
+    for (int k = 0, base = 0; base < num_seqs; ++k, base += PLAN_THREADS) {
+        const int i = base + tid;
+        int L = 0, n = 0, len = 0;
+        if (i < num_seqs) {
+            if (k < PLAN_REG) {
+                L = lreg[0];
+#pragma unroll
+                for (int r = 1; r < PLAN_REG; ++r)
+                    if (r == k) L = lreg[r];
+            } else {
+                L = clen(i);
+            }
+            const int tiles = (L + DECODE_TILE - 1) / DECODE_TILE;
+            if (tiles > 0) {
+                n = max(max(1, (tiles + target / 2) / target), (tiles + max_tiles - 1) / max_tiles);
+                const int lt = (tiles + n - 1) / n;
+                n = (tiles + lt - 1) / lt;
+                len = lt * DECODE_TILE;
+            }
+        }
+        int chunk;
+        const int first = carry + plan_exclusive_scan(n, s_wave, &chunk);
+        const int4 si = make_int4(first, n, len, L);
+#pragma unroll
+        for (int r = 0; r < PLAN_REG; ++r)
+            if (r == k) sreg[r] = si;
+        if (i < num_seqs) {
+            seq_info[i] = si;
+            if (n > 0) {
+                my_max = max(my_max, min(len, L));
+            } else {                                  // empty context: zero outputs for every head
+                const int64_t words = (int64_t)out_row_elems * elem_bytes / 4;
+                uint32_t *o = (uint32_t *)((char *)out + (int64_t)i * out_row_elems * elem_bytes);
+                for (int64_t w = 0; w < words; ++w) o[w] = 0u;
+            }
+        }
+        carry += chunk;
+    }
+    if (tid == 0) ctrl[0] = carry;
+    my_max = wave_max(my_max);
+    if (wave_lead) atomicMax(&s_maxlen, my_max);
+    __syncthreads();
+    const int maxlen = s_maxlen;
+    auto bucket = [&](int ntok) {
+        return min(PLAN_BUCKETS - 1, (int)((int64_t)(maxlen - ntok) * PLAN_BUCKETS / maxlen));
+    };
+    auto count = [&](const int4 &si) {
+        if (si.y <= 0) return;
+        if (si.y > 1) atomicAdd(&hist[bucket(si.z)], si.y - 1);
+        atomicAdd(&hist[bucket(si.w - (si.y - 1) * si.z)], 1);
+    };
+#pragma unroll
+    for (int k = 0; k < PLAN_REG; ++k)
+        if (tid + k * PLAN_THREADS < num_seqs) count(sreg[k]);
+    for (int i = tid + PLAN_REG * PLAN_THREADS; i < num_seqs; i += PLAN_THREADS) count(seq_info[i]);
     __syncthreads();
     if (tid < 64) {                                   // exclusive scan of the 64 buckets in one wave
         const int h = hist[tid];
@@ -97,24 +215,19 @@ decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int m
             if (tid >= o) v += u;
         }
         offs[tid] = v - h;
-        if (tid == 63) ctrl[0] = v;
     }
     __syncthreads();
-    for (int i = tid; i < num_seqs; i += PLAN_THREADS) {
-        const int L = min(context_lens[i], max_context_len);
-        if (L <= 0) {                                 // empty context: zero outputs for every head
-            const int64_t n = (int64_t)out_row_elems * elem_bytes / 4;
-            uint32_t *o = (uint32_t *)((char *)out + (int64_t)i * out_row_elems * elem_bytes);
-            for (int64_t k = 0; k < n; ++k) o[k] = 0u;
-            continue;
-        }
-        const int nparts = (L + part_tokens - 1) / part_tokens;
-        for (int part = 0, start = 0; start < L; ++part, start += part_tokens) {
-            const int ntok = min(part_tokens, L - start);
-            const int pos = atomicAdd(&offs[bucket(ntok)], 1);
-            items[pos] = make_int4(i, part, ntok, nparts);
-        }
-    }
+    auto emit = [&](int i, const int4 &si) {      // n - 1 full parts share a bucket: one reservation
+        if (si.y <= 0) return;
+        const int pfull = si.y > 1 ? atomicAdd(&offs[bucket(si.z)], si.y - 1) : 0;
+        for (int p = 0; p + 1 < si.y; ++p) items[pfull + p] = make_int4(i, p * si.z, si.z, si.x + p);
+        const int start = (si.y - 1) * si.z;
+        items[atomicAdd(&offs[bucket(si.w - start)], 1)] = make_int4(i, start, si.w - start, si.y > 1 ? si.x + si.y - 1 : -1);
+    };
+#pragma unroll
+    for (int k = 0; k < PLAN_REG; ++k)
+        if (tid + k * PLAN_THREADS < num_seqs) emit(tid + k * PLAN_THREADS, sreg[k]);
+    for (int i = tid + PLAN_REG * PLAN_THREADS; i < num_seqs; i += PLAN_THREADS) emit(i, seq_info[i]);
 }
 
 template <bool BF16, int D, int G, int NV_, int R_, int NW_>
@@ -122,8 +235,8 @@ __global__ void __launch_bounds__(64 * NW_)
 decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x4 *__restrict__ key_cache,
               const u32x4 *__restrict__ value_cache, const int32_t *__restrict__ block_tables, int bt_stride,
               const int4 *__restrict__ items, const int *__restrict__ ctrl, int num_kv_heads,
-              int64_t num_blocks, int log2_bs, int part_tokens, float scale_log2e,
-              float *__restrict__ ws_m, float *__restrict__ ws_l, float *__restrict__ ws_o, int max_parts) {
+              int64_t num_blocks, int log2_bs, float scale_log2e,
+              float *__restrict__ ws_m, float *__restrict__ ws_l, float *__restrict__ ws_o) {
     using S = DecodeShape<BF16, D, G, NV_, R_, NW_>;
     constexpr int NV = S::NV, LPT = S::LPT, RPW = S::RPW, R = S::R, TILE = S::TILE, EPL = S::EPL, VEC = S::VEC;
     constexpr int NW = S::NW;
@@ -132,18 +245,17 @@ decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x
     const int grp = lane / LPT, sub = lane % LPT;
     const int num_heads = num_kv_heads * G;
 
-    // work item in longest-first order; slots past the list exit
-    const int slot = blockIdx.x;
-    if (slot >= ctrl[0] * num_kv_heads) return;
-    const int4 item = items[slot / num_kv_heads];
-    const int kvh = slot % num_kv_heads;
-    const int seq = item.x, part = item.y, ntok = item.z, nparts = item.w;
-    const bool several = nparts > 1;
+    // unit in longest-first order; workgroups past the list exit
+    const int unit = blockIdx.x;
+    if (unit >= ctrl[0] * num_kv_heads) return;
+    const int4 item = items[unit / num_kv_heads];
+    const int kvh = unit % num_kv_heads;
+    const int seq = item.x, start = item.y, ntok = item.z, pslot = item.w;
+    const bool several = pslot >= 0;
 
-    // the partition's block-table slice, one id per lane (partitions never pass the table's stride)
-    const int start = part * part_tokens;
+    // the part's block-table slice (<= 64 ids), one id per lane
     const int first_blk = start >> log2_bs;
-    const int nbp = part_tokens >> log2_bs;
+    const int nbp = ((start + ntok - 1) >> log2_bs) - first_blk + 1;
     int my_blk = -1;
     if (lane < nbp && first_blk + lane < bt_stride) my_blk = block_tables[(int64_t)seq * bt_stride + first_blk + lane];
     const int bs_mask = (1 << log2_bs) - 1;
@@ -364,7 +476,7 @@ decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x
                 if constexpr (BF16) ((uint16_t *)out)[o] = (uint16_t)f32_to_bf16_rne(oo / ll);
                 else ((float *)out)[o] = oo / ll;
             } else {
-                const int64_t pidx = ((int64_t)seq * num_heads + head) * max_parts + part;
+                const int64_t pidx = (int64_t)pslot * num_heads + head;
                 ws_o[pidx * D + d] = oo;
                 if (d == 0) {
                     ws_m[pidx] = mm;
@@ -395,7 +507,7 @@ decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x
                     }
                 }
             } else {
-                const int64_t pidx = ((int64_t)seq * num_heads + head) * max_parts + part;
+                const int64_t pidx = (int64_t)pslot * num_heads + head;
 #pragma unroll
                 for (int v = 0; v < NV; ++v)
 #pragma unroll
@@ -412,75 +524,371 @@ decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x
     }
 }
 
-// Merge the partitions of each (sequence, head): M = max_p m_p, w_p = 2^(m_p - M),
-// out = sum_p w_p o_p / sum_p w_p l_p. One workgroup per (kv head, sequence) serves its G heads:
-// wave-level reductions give M and the denominator per head, then each thread merges (head, dim)
-// outputs with loads coalesced along dim. Sequences that fit one partition were written by the
-// decode kernel and exit at once.
-constexpr int REDUCE_THREADS = 256;
+// Buffer descriptor word 3 for raw (untyped, unswizzled) buffers on gfx9-family GPUs.
+constexpr int BUF_RSRC_W3 = 0x00020000;
 
-template <bool BF16, int D, int G>
-__global__ void __launch_bounds__(REDUCE_THREADS)
-decode_reduce_kernel(void *__restrict__ out, const int32_t *__restrict__ context_lens, int max_context_len,
-                     int num_kv_heads, int part_tokens, const float *__restrict__ ws_m, const float *__restrict__ ws_l,
-                     const float *__restrict__ ws_o, int max_parts) {
-    __shared__ float s_max[G], s_inv[G];
-    const int kvh = blockIdx.x, seq = blockIdx.y;
-    const int L = min(context_lens[seq], max_context_len);
-    const int nparts = (L + part_tokens - 1) / part_tokens;
-    if (nparts <= 1) return;
+// 16-byte load through a buffer descriptor; non-temporal unless PKV_DECODE_NT is 0.
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, PKV_DECODE_NT ? 2 : 0);
+}
+
+// The same units on the matrix cores (bf16, head_dim 128, block_size >= 16), with a persistent grid:
+// one workgroup of one wave per resident wave slot, each taking units from the list until it is done.
+// The G query heads of the kv head are the N = 16 columns of v_mfma_f32_16x16x32_bf16 (columns past
+// G carry zero queries and are never written), so a 32-token tile costs 8 MFMAs per product and the
+// vector ALU keeps only the softmax.
+// A tile is two 16-token groups g. Lane l = n + 16 b (n = l % 16, b = l / 16) holds:
+//   K (A operand of S^T = K Q^T): token 16 g + n, dims 32 c + 8 b .. +8 for c = 0..3 (each load covers
+//     64 contiguous bytes of 16 rows);
+//   Q (B operand): head n, the same dims (zero for n >= G);
+//   S^T (output): head n, tokens 16 g + 4 b + i, i = 0..3;
+//   V: tokens 16 g + 4 b + i, dims 8 n .. 8 n + 8 (each load covers 4 whole rows);
+//   P^T (B operand of O^T = V^T P^T): the rounded weights of the lane's own S^T values, reduction
+//     element e = 4 g + i <-> token 16 g + 4 b + i;
+//   V^T (A operand, one MFMA per j = 0..7): row n <-> dim 8 n + j, element e = element j of the lane's V
+//     row of token (g, i), paired with v_perm: the data never leaves the lane;
+//   O^T (output of MFMA j): head n, dims 8 (4 b + i) + j, so the lane ends with dims 32 b .. 32 b + 32.
+// The running max of a head is shared by its 4 lanes (max over lane ^ 16, lane ^ 32); the running sum
+// is kept per lane and summed when the unit ends.
+// The K/V pipeline runs across unit boundaries: while the last tile of a unit is computed, the first
+// tile of the wave's next unit is already loading (its work item and block-table slice were fetched
+// during the current unit), so a wave pays the dependent-load chain of a unit start only once.
+// Block size >= 16 puts each 16-token group in one block: the block id and block base are wave-uniform
+// and lanes add 32-bit row offsets.
+template <int G>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x4 *__restrict__ key_cache,
+                   const u32x4 *__restrict__ value_cache, const int32_t *__restrict__ block_tables, int bt_stride,
+                   const int4 *__restrict__ items, const int *__restrict__ ctrl, int num_kv_heads,
+                   int64_t num_blocks, int log2_bs, float scale_log2e,
+                   float *__restrict__ ws_m, float *__restrict__ ws_l, float *__restrict__ ws_o) {
+    static_assert(G >= 1 && G <= 16, "query heads per kv head");
+    constexpr int D = 128, CH = D / 8;        // 16-byte chunks per row
+    constexpr int TILE = 32;
+    const int lane = threadIdx.x, n = lane & 15, b = lane >> 4;
     const int num_heads = num_kv_heads * G;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int h = wave; h < G; h += REDUCE_THREADS / 64) {
-        const int64_t pbase = ((int64_t)seq * num_heads + kvh * G + h) * max_parts;
-        float mm = M_INIT;
-        for (int p = lane; p < nparts; p += 64) mm = fmaxf(mm, ws_m[pbase + p]);
-        for (int o = 32; o >= 1; o >>= 1) mm = fmaxf(mm, __shfl_xor(mm, o));
-        float ll = 0.f;
-        for (int p = lane; p < nparts; p += 64) ll += ws_l[pbase + p] * fast_exp2(ws_m[pbase + p] - mm);
-        for (int o = 32; o >= 1; o >>= 1) ll += __shfl_xor(ll, o);
-        if (lane == 0) {
-            s_max[h] = mm;
-            s_inv[h] = 1.0f / ll;
+    const int bs_mask = (1 << log2_bs) - 1;
+    const int nunits = ctrl[0] * num_kv_heads;
+    const int W = gridDim.x;
+    if ((int)blockIdx.x >= nunits) return;
+    // Units are taken from the longest-first list in strata of W: in stratum k wave w takes unit
+    // k W + w for even k and k W + W - 1 - w for odd k (snake order, so the long units of one stratum
+    // pair with the short ones of the next); a wave stops at its first index past the list.
+    auto unit_index = [&](int k) { return k * W + ((k & 1) ? W - 1 - (int)blockIdx.x : (int)blockIdx.x); };
+
+    struct Unit {
+        int seq, start, ntok, pslot, kvh, first_blk, ntiles;
+    };
+    auto load_unit = [&](int uu) {
+        const int4 it = items[uu / num_kv_heads];
+        Unit x;
+        x.seq = it.x;
+        x.start = it.y;
+        x.ntok = it.z;
+        x.pslot = it.w;
+        x.kvh = uu % num_kv_heads;
+        x.first_blk = it.y >> log2_bs;
+        x.ntiles = (it.z + TILE - 1) / TILE;
+        return x;
+    };
+    // the unit's block-table slice (<= 64 ids), one id per lane
+    auto load_slice = [&](const Unit &x) {
+        const int span = ((x.start + x.ntok - 1) >> log2_bs) - x.first_blk + 1;
+        int v = -1;
+        if (lane < span && x.first_blk + lane < bt_stride) v = block_tables[(int64_t)x.seq * bt_stride + x.first_blk + lane];
+        return v;
+    };
+    u32x4 qt[4];
+    auto load_q = [&](const Unit &x) {
+        const u32x4 *qv = (const u32x4 *)query;
+        const int64_t row = ((int64_t)x.seq * num_heads + x.kvh * G + (n < G ? n : 0)) * CH;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qt[c] = n < G ? qv[row + 4 * c + b] : u32x4{0, 0, 0, 0};
+    };
+
+    struct Tile {
+        u32x4 k[2][4];
+        u32x4 v[2][4];
+        bool live[2];                           // group holds at least one token and a valid block id
+    };
+    // Rows past the unit's end are clamped to its last token (same block: a group past the end is
+    // clamped whole), so every lane reads a row holding finite data; such tokens get zero weight.
+    // Loads go through buffer descriptors of the group's (block, kv head) slab: wave-uniform base,
+    // 32-bit lane offsets, and the hardware range check bounds every access to the slab.
+    const uint32_t slab_bytes = (uint32_t)CH * 16u << log2_bs;
+    auto issue = [&](const Unit &x, int xblk, int tile, Tile &t) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int tl0 = tile * TILE + 16 * g;
+            const int tlc = min(tl0, x.ntok - 1);
+            const int tokc = x.start + tlc;
+            const int64_t blk = __builtin_amdgcn_readlane(xblk, (tokc >> log2_bs) - x.first_blk);
+            t.live[g] = blk >= 0 && blk < num_blocks;
+            const int64_t slab = t.live[g] ? ((blk * num_kv_heads + x.kvh) << log2_bs) * CH : 0;
+            const __amdgpu_buffer_rsrc_t kr =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(key_cache + slab), (short)0, (int)slab_bytes, BUF_RSRC_W3);
+            const __amdgpu_buffer_rsrc_t vr =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(value_cache + slab), (short)0, (int)slab_bytes, BUF_RSRC_W3);
+            const int last = x.ntok - 1 - tl0;              // rows past it are clamped to it
+            const int r0 = (tokc & bs_mask) - tlc + tl0;    // slab row of token tl0
+            const int koff = ((r0 + min(n, last)) * CH + b) * 16;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) t.k[g][c] = buffer_load16(kr, koff + 64 * c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t.v[g][i] = buffer_load16(vr, ((r0 + min(4 * b + i, last)) * CH + n) * 16);
         }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += REDUCE_THREADS) {
-        const int h = idx / D, d = idx % D;
-        const int64_t pbase = ((int64_t)seq * num_heads + kvh * G + h) * max_parts;
-        const float mm = s_max[h];
-        float oo = 0.f;
-        for (int p = 0; p < nparts; ++p) oo += ws_o[(pbase + p) * D + d] * fast_exp2(ws_m[pbase + p] - mm);
-        const float res = oo * s_inv[h];
-        const int64_t o = ((int64_t)seq * num_heads + kvh * G + h) * D + d;
-        if constexpr (BF16) ((uint16_t *)out)[o] = (uint16_t)f32_to_bf16_rne(res);
-        else ((float *)out)[o] = res;
+    };
+
+    float m = M_INIT, l = 0.f;
+    f32x4 acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const Unit &x, int tile, Tile &t) {
+        // masked tokens: past the unit's end (only in its last tile), or in a block outside the pool,
+        // whose rows (block 0) may hold anything: those get V zeroed as well
+        const bool partial = (tile + 1) * TILE > x.ntok || !t.live[0] || !t.live[1];   // wave-uniform
+        if (!t.live[0] || !t.live[1]) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (!t.live[g]) t.v[g][i] = u32x4{0, 0, 0, 0};
+        }
+        f32x4 s[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            s[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) s[g] = mfma16x16x32(t.k[g][c], qt[c], s[g]);
+        }
+        float xs[2][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = !partial || (t.live[g] && tile * TILE + 16 * g + 4 * b + i < x.ntok);
+                xs[g][i] = ok ? s[g][i] * scale_log2e : -INFINITY;
+                mx = fmaxf(mx, xs[g][i]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx);
+        if (__builtin_amdgcn_ballot_w64(m_new > m)) {   // rescale only when a running max grew
+            const float alpha = fast_exp2(m - m_new);
+            m = m_new;
+            l *= alpha;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+        }
+        constexpr uint32_t ONES = 0x3f803f80u;
+        u32x4 pb;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            pb[2 * g] = pack_bf16x2(fast_exp2(xs[g][0] - m), fast_exp2(xs[g][1] - m));
+            pb[2 * g + 1] = pack_bf16x2(fast_exp2(xs[g][2] - m), fast_exp2(xs[g][3] - m));
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) l = dot2_bf16(pb[w], ONES, l);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int w = j >> 1;
+            u32x4 a;
+            if (j & 1) {
+                a[0] = pair_hi(t.v[0][0][w], t.v[0][1][w]);
+                a[1] = pair_hi(t.v[0][2][w], t.v[0][3][w]);
+                a[2] = pair_hi(t.v[1][0][w], t.v[1][1][w]);
+                a[3] = pair_hi(t.v[1][2][w], t.v[1][3][w]);
+            } else {
+                a[0] = pair_lo(t.v[0][0][w], t.v[0][1][w]);
+                a[1] = pair_lo(t.v[0][2][w], t.v[0][3][w]);
+                a[2] = pair_lo(t.v[1][0][w], t.v[1][1][w]);
+                a[3] = pair_lo(t.v[1][2][w], t.v[1][3][w]);
+            }
+            acc[j] = mfma16x16x32(a, pb, acc[j]);
+        }
+    };
+
+    // write the unit's result (final output, or its partial slot) and reset the softmax state
+    auto finish = [&](const Unit &x) {
+        float lt = l + __shfl_xor(l, 16);
+        lt += __shfl_xor(lt, 32);
+        if (n < G) {
+            const int head = x.kvh * G + n;
+            if (x.pslot < 0) {
+                const float inv = 1.0f / lt;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    u32x4 pk;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) pk[w] = pack_bf16x2(acc[2 * w][i] * inv, acc[2 * w + 1][i] * inv);
+                    *(u32x4 *)((uint16_t *)out + ((int64_t)x.seq * num_heads + head) * D + 32 * b + 8 * i) = pk;
+                }
+            } else {
+                const int64_t pidx = (int64_t)x.pslot * num_heads + head;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float *o = ws_o + pidx * D + 32 * b + 8 * i;
+                    *(f32x4 *)o = f32x4{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+                    *(f32x4 *)(o + 4) = f32x4{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+                }
+                if (b == 0) {
+                    ws_m[pidx] = m;
+                    ws_l[pidx] = lt;
+                }
+            }
+        }
+        m = M_INIT;
+        l = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+
+    Unit cur = load_unit(blockIdx.x);
+    int cur_blk = load_slice(cur);
+    load_q(cur);
+    int k = 1;                                  // stratum of `nxt`
+    Unit nxt = cur;
+    bool has_next = unit_index(k) < nunits;
+    if (has_next) nxt = load_unit(unit_index(k));
+    int nxt_blk = -1;
+    bool nxt_ready = false;
+    int ct = 0;                                 // tile of `cur` being computed
+
+    // one pipeline step: load the tile after `ct` into B (the next unit's first tile when `ct` is the
+    // last), compute tile `ct` from A, then advance; false once the wave's last unit is written
+    // (one issue site: after the wave's last tile it reloads that tile, which nothing reads)
+    auto step = [&](Tile &A, Tile &B) -> bool {
+        const bool last = ct + 1 >= cur.ntiles;
+        const bool go_next = last && has_next;
+        if (go_next && !nxt_ready) {
+            nxt_blk = load_slice(nxt);
+            nxt_ready = true;
+        }
+        issue(go_next ? nxt : cur, go_next ? nxt_blk : cur_blk, go_next ? 0 : (last ? ct : ct + 1), B);
+        compute(cur, ct, A);
+        if (!last) {
+            ++ct;
+        } else {
+            finish(cur);
+            if (!has_next) return false;
+            cur = nxt;
+            cur_blk = nxt_blk;
+            ct = 0;
+            load_q(cur);
+            nxt_ready = false;
+            ++k;
+            has_next = unit_index(k) < nunits;
+            if (has_next) nxt = load_unit(unit_index(k));
+        }
+        if (has_next && !nxt_ready && ct > 0) {   // the next unit's item has had a step to arrive
+            nxt_blk = load_slice(nxt);
+            nxt_ready = true;
+        }
+        return true;
+    };
+
+    Tile ta, tb;
+    issue(cur, cur_blk, 0, ta);
+    while (step(ta, tb) && step(tb, ta)) {
     }
 }
 
-template <bool BF16, int D, int G, int NV, int R, int NW>
+// Merge the parts of each (sequence, head): M = max_p m_p, w_p = 2^(m_p - M),
+// out = sum_p w_p o_p / sum_p w_p l_p. A workgroup serves `hpb` heads of one sequence (hpb in {1, 2, 4, 8},
+// chosen so the grid has a few thousand workgroups: with many sequences most have one part and their
+// workgroups exit after one load). Its threads are hpb heads x PL = 8 / hpb part lanes x D/4 dim groups:
+// a thread sums dims 4 dg .. +4 over the parts p = pl mod PL with 16-byte loads, and the part lanes are
+// added through LDS. Sequences of one part were written by the decode kernel.
+constexpr int REDUCE_THREADS = 256;
+
+template <bool BF16, int D>
+__global__ void __launch_bounds__(REDUCE_THREADS)
+decode_reduce_kernel(void *__restrict__ out, const int4 *__restrict__ seq_info, int num_heads, int hpb,
+                     const float *__restrict__ ws_m, const float *__restrict__ ws_l, const float *__restrict__ ws_o) {
+    constexpr int DG = D / 4, SLOTS = REDUCE_THREADS / DG;          // SLOTS = head slots x part lanes
+    __shared__ f32x4 s_o[SLOTS][DG];
+    __shared__ float s_l[SLOTS];
+    const int seq = blockIdx.y;
+    const int4 si = seq_info[seq];
+    const int nparts = si.y;
+    if (nparts <= 1) return;
+    const int PL = SLOTS / hpb;
+    const int t = threadIdx.x, slot = t / DG, dg = t % DG;
+    const int hs = slot / PL, pl = slot % PL;
+    const int head = blockIdx.x * hpb + hs;
+    const bool active = head < num_heads;
+    float ll = 0.f;
+    f32x4 oo = {0.f, 0.f, 0.f, 0.f};
+    if (active) {
+        const int64_t p0 = (int64_t)si.x * num_heads + head;     // part p sits at p0 + p * num_heads
+        float mm = M_INIT;
+#pragma unroll 8
+        for (int p = 0; p < nparts; ++p) mm = fmaxf(mm, ws_m[p0 + (int64_t)p * num_heads]);
+#pragma unroll 2
+        for (int p = pl; p < nparts; p += PL) {
+            const int64_t pi = p0 + (int64_t)p * num_heads;
+            const float w = fast_exp2(ws_m[pi] - mm);
+            ll += ws_l[pi] * w;
+            oo += w * *(const f32x4 *)(ws_o + pi * D + 4 * dg);
+        }
+    }
+    s_o[slot][dg] = oo;
+    if (dg == 0) s_l[slot] = ll;
+    __syncthreads();
+    if (pl != 0 || !active) return;
+    for (int q = 1; q < PL; ++q) {
+        oo += s_o[slot + q][dg];
+        ll += s_l[slot + q];
+    }
+    const float inv = 1.0f / ll;
+    const int64_t o = ((int64_t)seq * num_heads + head) * D + 4 * dg;
+    if constexpr (BF16) {
+        *(uint2 *)((uint16_t *)out + o) = make_uint2(pack_bf16x2(oo[0] * inv, oo[1] * inv), pack_bf16x2(oo[2] * inv, oo[3] * inv));
+    } else {
+        *(f32x4 *)((float *)out + o) = oo * inv;
+    }
+}
+
+template <bool BF16, int D, int G, int NV, int R, int NW, bool MFMA>
 static hipError_t launch_decode_cfg(const DecodeArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, a.context_lens, a.num_seqs,
-                       a.max_context_len, a.part_tokens, a.items, a.ctrl, a.out, a.num_kv_heads * G * D,
-                       BF16 ? 2 : 4);
+                       a.max_context_len, a.num_kv_heads, a.target_units, a.max_part_tiles, a.min_part_tiles, a.items,
+                       a.seq_info, a.ctrl, a.out, a.num_kv_heads * G * D, BF16 ? 2 : 4);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t slots = (int64_t)a.num_seqs * a.num_parts * a.num_kv_heads;
-    hipLaunchKernelGGL((decode_kernel<BF16, D, G, NV, R, NW>), dim3((unsigned)slots), dim3(64 * NW), 0, stream, a.out,
-                       a.query, (const u32x4 *)a.key_cache, (const u32x4 *)a.value_cache, a.block_tables,
-                       a.bt_stride, a.items, a.ctrl, a.num_kv_heads, a.num_blocks, a.log2_bs, a.part_tokens,
-                       a.scale_log2e, a.ws_m, a.ws_l, a.ws_o, a.num_parts);
+    const int64_t units = (int64_t)a.max_items * a.num_kv_heads;     // upper bound on the unit count
+    if constexpr (MFMA) {
+        static_assert(BF16 && D == 128, "matrix-core decode: bf16, head_dim 128");
+        const int64_t grid = units < a.workers ? units : a.workers;
+        hipLaunchKernelGGL((decode_mfma_kernel<G>), dim3((unsigned)grid), dim3(64), 0, stream, a.out, a.query,
+                           (const u32x4 *)a.key_cache, (const u32x4 *)a.value_cache, a.block_tables, a.bt_stride,
+                           a.items, a.ctrl, a.num_kv_heads, a.num_blocks, a.log2_bs, a.scale_log2e, a.ws_m, a.ws_l,
+                           a.ws_o);
+    } else {
+        hipLaunchKernelGGL((decode_kernel<BF16, D, G, NV, R, NW>), dim3((unsigned)units), dim3(64 * NW), 0, stream,
+                           a.out, a.query, (const u32x4 *)a.key_cache, (const u32x4 *)a.value_cache, a.block_tables,
+                           a.bt_stride, a.items, a.ctrl, a.num_kv_heads, a.num_blocks, a.log2_bs, a.scale_log2e,
+                           a.ws_m, a.ws_l, a.ws_o);
+    }
     e = hipGetLastError();
-    if (e != hipSuccess || a.num_parts <= 1) return e;
-    hipLaunchKernelGGL((decode_reduce_kernel<BF16, D, G>), dim3(a.num_kv_heads, a.num_seqs), dim3(REDUCE_THREADS), 0,
-                       stream, a.out, a.context_lens, a.max_context_len, a.num_kv_heads, a.part_tokens, a.ws_m, a.ws_l,
-                       a.ws_o, a.num_parts);
+    if (e != hipSuccess) return e;
+    // heads per reduce workgroup: the fewest (1..8) that keep the grid at ~2048 workgroups or more
+    const int num_heads = a.num_kv_heads * G;
+    int hpb = 8;
+    while (hpb > 1 && (int64_t)((num_heads + hpb - 1) / hpb) * a.num_seqs < 2048) hpb >>= 1;
+    hipLaunchKernelGGL((decode_reduce_kernel<BF16, D>), dim3((num_heads + hpb - 1) / hpb, a.num_seqs),
+                       dim3(REDUCE_THREADS), 0, stream, a.out, a.seq_info, num_heads, hpb, a.ws_m, a.ws_l, a.ws_o);
     return hipGetLastError();
 }
 
 // Kernel shape per (dtype, head_dim, group): vectors per lane NV, tile depth R, waves per workgroup NW.
 #ifndef PKV_DECODE_NW
 #define PKV_DECODE_NW 1
+#endif
+#ifndef PKV_DECODE_MFMA_MIN_G
+#define PKV_DECODE_MFMA_MIN_G 1  // bf16 head_dim 128 with at least this many query heads per kv head: MFMA
 #endif
 #ifndef PKV_DECODE_R2
 #define PKV_DECODE_R2 2      // tile depth when a lane holds two vectors of a row
@@ -490,7 +898,10 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     constexpr int VPR = D / (BF16 ? 8 : 4);
     constexpr int NV = (VPR / ((G <= 4) ? 2 : 1) > 16) ? VPR / 16 : ((G <= 4) ? 2 : 1);
     constexpr int R = (NV == 1) ? 2 * PKV_DECODE_R2 : (NV == 2 ? PKV_DECODE_R2 : 1);
-    return launch_decode_cfg<BF16, D, G, NV, R, PKV_DECODE_NW>(a, stream);
+    if constexpr (BF16 && D == 128 && G >= PKV_DECODE_MFMA_MIN_G) {
+        if (a.log2_bs >= 4) return launch_decode_cfg<BF16, D, G, NV, R, PKV_DECODE_NW, true>(a, stream);
+    }
+    return launch_decode_cfg<BF16, D, G, NV, R, PKV_DECODE_NW, false>(a, stream);
 }
 
 template <bool BF16, int D>
@@ -517,5 +928,6 @@ hipError_t launch_decode(const DecodeArgs &a, bool bf16, int head_dim, int group
 }
 
 int decode_max_part_blocks() { return MAX_PART_BLOCKS; }
+int decode_tile_tokens() { return DECODE_TILE; }
 
 }  // namespace pkv

@@ -90,4 +90,14 @@ __device__ __forceinline__ void group_sum_all(float *v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// D = A B + C on one 16x16x32 bf16 MFMA (fp32 accumulate). Lane l supplies A[l%16][8*(l/16) .. +8]
+// and B[8*(l/16) .. +8][l%16] (8 bf16 each, element order = reduction order) and holds
+// D[4*(l/16) + i][l%16], i = 0..3.
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
+
 }  // namespace pkv

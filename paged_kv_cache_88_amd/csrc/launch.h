@@ -32,18 +32,23 @@ struct DecodeArgs {
     int num_kv_heads;
     int64_t num_blocks;    // tokens whose block id lies outside [0, num_blocks) are skipped
     int log2_bs;
-    int part_tokens;       // tokens per partition, a multiple of the block size
-    int num_parts;         // ceil(max_context_len / part_tokens), >= 1
+    int workers;           // resident one-wave workgroups (persistent grid size)
+    int target_units;      // units the plan aims to cut the batch into
+    int max_part_tiles;    // longest part, in 32-token tiles (its table slice must fit 64 lanes)
+    int min_part_tiles;    // shortest part a sequence is split into, in tiles
+    int64_t max_items;     // bound on the number of parts (sizes the work list and partials)
     float scale_log2e;
-    int4 *items;           // work list, [num_seqs * num_parts]
-    int *ctrl;             // ctrl[0] = number of work items
-    float *ws_m;           // [num_seqs][num_heads][num_parts]   (used when num_parts > 1)
-    float *ws_l;           // [num_seqs][num_heads][num_parts]
-    float *ws_o;           // [num_seqs][num_heads][num_parts][head_dim]
+    int4 *items;           // work list, [max_items]
+    int4 *seq_info;        // [num_seqs]: first partial slot, parts, part length, length
+    int *ctrl;             // ctrl[0] = number of parts
+    float *ws_m;           // [max_items][num_heads]
+    float *ws_l;           // [max_items][num_heads]
+    float *ws_o;           // [max_items][num_heads][head_dim]
 };
 
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, int head_dim, int group, hipStream_t stream);
 int decode_max_part_blocks();
+int decode_tile_tokens();
 
 struct PrefillArgs {
     void *out;

@@ -38,7 +38,6 @@
 
 namespace pkv {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int PF_THREADS = 256;
@@ -50,11 +49,6 @@ constexpr int PF_KPAD = PF_D + 8;         // LDS row stride of K, bf16 elements 
 constexpr int PF_VPAD = PF_BN + 4;        // LDS row stride of V^T (136 bytes: 16 rows fall on distinct bank pairs)
 constexpr float PF_M_INIT = -1.0e30f;
 constexpr int PF_XCDS = 8;                // MI355X: 8 XCDs, each with its own L2
-
-__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                   c, 0, 0, 0);
-}
 
 template <int G>
 __global__ void __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))

@@ -91,11 +91,22 @@ def test_decode_validation(lib):
     assert call(1, None, None, None, None, None, 4, None, 0, 10, 8, 2, 128, 16, 64, 0.1, None, 0, None) == 0
 
 
+def _max_parts(b, hkv, bs, max_len):
+    """Bound on the parts the device plan cuts a batch into (it aims at one unit for each of at most 2048
+    resident waves; a part's block-table slice fits 64 lanes, 63 blocks when parts may start inside a
+    block)."""
+    max_tiles = (64 if bs <= 32 else 63) * bs // 32
+    return 2 * b + -(-2048 // hkv) + -(-b * -(-max_len // 32) // max_tiles)
+
+
 def test_decode_workspace_size(lib):
     f = lib.pkv_paged_attention_decode_workspace_size
-    one = f(64, 32, 8, 128, 16, 512)                # one partition: control word + work list only
-    assert 0 < one < 4096
-    assert f(16, 64, 8, 128, 256, 32768) >= 16 * 64 * 32 * 130 * 4     # partials of 32 partitions
+    for b, h, hkv, d, bs, max_len in [(64, 32, 8, 128, 16, 512), (16, 64, 8, 128, 256, 32768), (1, 8, 1, 64, 1, 77)]:
+        parts = _max_parts(b, hkv, bs, max_len)
+        # work list, per-sequence info and fp32 partials (m, l, head_dim accumulators) of every part
+        need = parts * 16 + b * 16 + parts * h * (d + 2) * 4
+        got = f(b, h, hkv, d, bs, max_len)
+        assert need <= got <= need + 6 * 256
     assert f(0, 32, 8, 128, 16, 512) == 0
 
 

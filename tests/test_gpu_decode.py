@@ -35,7 +35,7 @@ EDGE_LENS = [1, 15, 16, 17, 33, 255, 256, 257, 511, 512, 513, 1025]
 
 @pytest.mark.parametrize("dtype", [W.F32, W.BF16])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("group", [1, 3, 4, 8])
+@pytest.mark.parametrize("group", [1, 3, 4, 6, 7, 8])
 @pytest.mark.parametrize("bs", [1, 16, 256])
 def test_edge_lengths(pkv, orc, dtype, d, group, bs):
     """Lengths around block and partition boundaries (single-pass and split paths), several GQA groups."""
