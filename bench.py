@@ -171,7 +171,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported (use --gpus 1).",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (use --gpus 1).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -47,6 +47,54 @@ def test_edge_lengths(pkv, orc, dtype, d, group, bs):
     assert_close(got, ref, dtype, f"{dtype} d{d} g{group} bs{bs}")
 
 
+@pytest.mark.parametrize("num_seqs", [1500, 5000])
+def test_many_sequences(pkv, orc, num_seqs):
+    """More sequences than the plan workgroup has threads (chunked scan) and than it keeps in registers:
+    short lognormal contexts with a few empty ones; the oracle checks a seeded sample and every empty one."""
+    rng = np.random.default_rng(num_seqs)
+    lens = np.clip(np.round(np.exp(np.log(40) + rng.standard_normal(num_seqs))), 0, 400).astype(np.int32)
+    lens[rng.choice(num_seqs, 5, replace=False)] = 0
+    nb = int(sum(W.blocks_for_tokens(int(n), 16) for n in lens)) + 4
+    c = W.make_decode_case("many", num_seqs, W.BF16, lens, 32, 8, 128, 16, nb, rng=rng)
+    got, _, _ = run_decode_case(pkv, c)
+    seqs = np.array(sorted(set(rng.choice(num_seqs, 40, replace=False).tolist()) | set(np.flatnonzero(lens == 0).tolist()) |
+                           {int(np.argmax(lens))}), np.int32)
+    assert_close(got[seqs], oracle_decode_case(orc, c, seqs=seqs), W.BF16, f"{num_seqs} sequences")
+    assert np.all(got[lens == 0] == 0)
+
+
+@pytest.mark.parametrize("dtype,d,group", [(W.BF16, 128, 8), (W.BF16, 128, 1), (W.F32, 64, 4)])
+def test_single_long_sequence(pkv, orc, dtype, d, group):
+    """One sequence: the plan cuts it into many parts (one per resident wave slot or so) merged by the
+    reduce kernel; every output checked."""
+    L = 30011
+    c = W.make_decode_case("long", 31, dtype, [L], 2 * group, 2, d, 256, W.blocks_for_tokens(L, 256) + 2)
+    got, _, _ = run_decode_case(pkv, c)
+    assert_close(got, oracle_decode_case(orc, c), dtype, f"{dtype} d{d} g{group}")
+
+
+@pytest.mark.parametrize("bs", [32, 64, 128])
+def test_parts_inside_blocks(pkv, orc, bs):
+    """Block sizes above the 32-token part granularity: parts start inside a block."""
+    lens = [5000, 4097, 3, 2500, 777]
+    nb = sum(W.blocks_for_tokens(n, bs) for n in lens) + 3
+    c = W.make_decode_case("midblock", bs, W.BF16, lens, 32, 8, 128, bs, nb)
+    got, _, _ = run_decode_case(pkv, c)
+    assert_close(got, oracle_decode_case(orc, c), W.BF16, f"bs{bs}")
+
+
+def test_mixed_long_and_short(pkv, orc):
+    """A few long contexts among many short ones: long ones split, short ones stay whole."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(1, 200, size=300).astype(np.int32)
+    lens[[3, 100, 250]] = [20000, 9000, 16384]
+    nb = int(sum(W.blocks_for_tokens(int(n), 16) for n in lens)) + 2
+    c = W.make_decode_case("mixed", 77, W.BF16, lens, 64, 8, 128, 16, nb, rng=rng)
+    got, _, _ = run_decode_case(pkv, c)
+    seqs = np.array(sorted({3, 100, 250} | set(rng.choice(300, 20, replace=False).tolist())), np.int32)
+    assert_close(got[seqs], oracle_decode_case(orc, c, seqs=seqs), W.BF16, "mixed")
+
+
 def test_empty_context_gives_zeros(pkv, orc):
     c = W.make_decode_case("empty", 7, W.BF16, [0, 5, 0, 600], 8, 2, 128, 16, 64)
     got, _, _ = run_decode_case(pkv, c)
