@@ -80,9 +80,10 @@ pkv_status pkv_kv_cache_store(pkv_dtype dtype, const void *key, const void *valu
 
 /*
  * Bytes of device workspace pkv_paged_attention_decode needs for these sizes (0 only when num_seqs is
- * 0): a work list of 16 bytes per (sequence, partition) plus, when max_context_len spans several
- * partitions, the partial softmax state (fp32 max, sum and head_dim accumulators per sequence, head
- * and partition) merged by a reduce pass.
+ * 0). The call cuts sequences into parts on the device, from the actual context_lens, so that the batch
+ * spreads evenly over the GPU; the size is the bound for any lengths up to max_context_len: a work list
+ * of 16 bytes per part, 16 bytes per sequence, and the partial softmax state of every part (fp32 max,
+ * sum and head_dim accumulators per head) that a reduce pass merges.
  */
 size_t pkv_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                                  int32_t head_dim, int32_t block_size, int32_t max_context_len);
@@ -92,9 +93,9 @@ size_t pkv_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_h
  *   out[i][h] = sum_{t < context_lens[i]} softmax_t(scale * query[i][h] . K_i[t]) V_i[t],
  * with K_i[t] = key_cache[block_tables[i][t / block_size]][h / G][t % block_size] and likewise V.
  * A sequence with context_lens[i] == 0 gets zeros. fp32 data computes in fp32. bf16 data: q.k and
- * p.v run on v_dot2_f32_bf16 with fp32 accumulation, the softmax weights of two tokens rounded to a
- * bf16 pair for p.v (their sum, the denominator, uses the same rounded weights); output rounded to
- * bf16 (nearest even).
+ * p.v take bf16 operands with fp32 accumulation (on MFMA for head_dim 128 and block_size >= 16, on
+ * v_dot2_f32_bf16 otherwise), the softmax weights rounded to bf16 for p.v (the denominator sums the same
+ * rounded weights); output rounded to bf16 (nearest even).
  * Source: "推理运行时", section 分页 KV (attention reads K/V through the block table);
  * "LLM Infra 101 v0.2: KV Cache", section 推理 (decode attends to the cache plus the new token).
  * block_tables: device int32 [num_seqs][block_table_stride]; context_lens: device int32 [num_seqs];
