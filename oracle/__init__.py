@@ -9,7 +9,7 @@ on tiny inputs and ``torch.nn.functional.scaled_dot_product_attention`` in float
 docstring for the passage it follows).
 
 Arrays use the storage conventions of ``workloads``: float32 arrays for fp32, uint16 bf16 bit
-patterns for bf16.
+patterns for bf16; "f64" (float64 arrays) serves dequantized int8 caches.
 """
 from __future__ import annotations
 
@@ -23,7 +23,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-_DT = {"f32": 0, "bf16": 1}
+_DT = {"f32": 0, "bf16": 1, "f64": 3}
 
 
 def build(force: bool = True, src: str = SRC, out: str = LIB) -> str:
@@ -49,7 +49,7 @@ def _c(a, dtype=None):
 
 
 def _store_dtype(dtype):
-    return np.float32 if dtype == "f32" else np.uint16
+    return {"f32": np.float32, "bf16": np.uint16, "f64": np.float64}[dtype]
 
 
 class Oracle:
@@ -66,7 +66,11 @@ class Oracle:
                                    P, I32, I32]
         lib.orc_prefill.argtypes = [ctypes.c_int, P, P, P, P, P, I32, P, P, I32, I32, I32, I32, I32, I64, D,
                                     I32, P, I32, I32]
-        for f in (lib.orc_store, lib.orc_gather, lib.orc_decode, lib.orc_prefill):
+        lib.orc_quantize_int8.argtypes = [ctypes.c_int, P, I64, I32, P, P]
+        lib.orc_store_int8.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, I64, I32, I32, I32, I64]
+        lib.orc_dequantize_int8.argtypes = [P, P, I64, I32, P]
+        for f in (lib.orc_store, lib.orc_gather, lib.orc_decode, lib.orc_prefill, lib.orc_quantize_int8,
+                  lib.orc_store_int8, lib.orc_dequantize_int8):
             f.restype = ctypes.c_int
         lib.orc_last_error.restype = ctypes.c_char_p
         lib.orc_max_threads.restype = ctypes.c_int
@@ -94,6 +98,43 @@ class Oracle:
         nb, hkv, bs, d = key_cache.shape
         self._check(self.lib.orc_store(_DT[dtype], _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
                                        _ptr(sm), len(sm), hkv, d, bs, nb))
+
+    def quantize_int8(self, dtype, rows):
+        """int8 codes and float32 scales of rows ``[..., D]`` (one scale per row): scale = max|x| / 127,
+        code = round-half-even(x / scale) clamped to [-127, 127], in float32; zero rows give scale 0."""
+        sd = _store_dtype(dtype)
+        r = _c(rows, sd)
+        d = r.shape[-1]
+        n = r.size // d
+        codes = np.zeros(r.shape, dtype=np.int8)
+        scales = np.zeros(r.shape[:-1], dtype=np.float32)
+        self._check(self.lib.orc_quantize_int8(_DT[dtype], _ptr(r), n, d, _ptr(codes), _ptr(scales)))
+        return codes, scales
+
+    def store_int8(self, dtype, key, value, key_cache, value_cache, key_scale, value_scale, slot_mapping):
+        """Quantize rows of key/value ``[N, Hkv, D]`` and scatter codes into the int8 caches
+        ``[NB, Hkv, bs, D]`` and scales into ``[NB, Hkv, bs]`` float32, in place (slots as in ``store``)."""
+        sd = _store_dtype(dtype)
+        for a, t in ((key_cache, np.int8), (value_cache, np.int8), (key_scale, np.float32), (value_scale, np.float32)):
+            if a.dtype != t or not a.flags.c_contiguous:
+                raise TypeError("int8 caches and float32 scales must be C-contiguous")
+        key, value = _c(key, sd), _c(value, sd)
+        sm = _c(slot_mapping, np.int32)
+        nb, hkv, bs, d = key_cache.shape
+        if key_scale.shape != (nb, hkv, bs) or value_scale.shape != (nb, hkv, bs):
+            raise ValueError("scale arrays must be [num_blocks, num_kv_heads, block_size]")
+        self._check(self.lib.orc_store_int8(_DT[dtype], _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                            _ptr(key_scale), _ptr(value_scale), _ptr(sm), len(sm), hkv, d, bs, nb))
+
+    def dequantize_int8(self, codes, scales):
+        """float64 values code * scale (exact) of int8 rows ``[..., D]`` with scales ``[...]``."""
+        c, sc = _c(codes, np.int8), _c(scales, np.float32)
+        d = c.shape[-1]
+        if sc.shape != c.shape[:-1]:
+            raise ValueError("one scale per row")
+        out = np.empty(c.shape, dtype=np.float64)
+        self._check(self.lib.orc_dequantize_int8(_ptr(c), _ptr(sc), c.size // d, d, _ptr(out)))
+        return out
 
     def copy_blocks(self, dtype, key_cache, value_cache, pairs):
         """In place: block pairs[k, 1] of both caches becomes a copy of block pairs[k, 0]."""
@@ -194,3 +235,15 @@ def decode(*a, **k):
 
 def prefill(*a, **k):
     return default().prefill(*a, **k)
+
+
+def quantize_int8(*a, **k):
+    return default().quantize_int8(*a, **k)
+
+
+def store_int8(*a, **k):
+    return default().store_int8(*a, **k)
+
+
+def dequantize_int8(*a, **k):
+    return default().dequantize_int8(*a, **k)

@@ -8,7 +8,9 @@
  * Layout it reads (chosen by the library and restated here independently):
  *   key_cache / value_cache : [num_blocks][num_kv_heads][block_size][head_dim]
  *   slot s                   : physical block s / block_size, offset s % block_size
- *   element dtype 0 = float32, 1 = bfloat16 (16-bit patterns, upcast exactly)
+ *   element dtype 0 = float32, 1 = bfloat16 (16-bit patterns, upcast exactly), 3 = float64
+ *   int8 cache (orc_store_int8): codes [num_blocks][num_kv_heads][block_size][head_dim] int8 and one
+ *   float32 scale per row, [num_blocks][num_kv_heads][block_size]
  *
  * Sources (web pages on the paged KV cache):
  *   - logical block j of a request lives in physical block block_table[j]; the kernel reads K/V
@@ -20,7 +22,10 @@
  *   - the decoded token attends to the cached tokens plus itself
  *     ("LLM Infra 101 v0.2: KV Cache", section 推理);
  *   - chunked prefill: a chunk attends to its cached prefix and to itself
- *     (Mini-SGLang 源码解析（二）, sections 6.6 and 6.9; "推理运行时", section Prefill 与 decode 输入).
+ *     (Mini-SGLang 源码解析（二）, sections 6.6 and 6.9; "推理运行时", section Prefill 与 decode 输入);
+ *   - a quantized cache keeps K/V as int8 instead of bf16, at some loss of accuracy
+ *     ("LLM Infra 101 v0.2: KV Cache", inference-engine list, KV Quantization). The pages fix no
+ *     scheme; the one restated here is symmetric, one scale per (token, kv head) row.
  * Attention itself is the textbook definition softmax(scale * q . k) weighted sum of v.
  */
 #include <math.h>
@@ -48,11 +53,12 @@ static int fail(const char *fmt, ...) {
 
 const char *orc_last_error(void) { return g_err; }
 
-static size_t elem_bytes(int dtype) { return dtype == 0 ? 4 : 2; }
+static size_t elem_bytes(int dtype) { return dtype == 0 ? 4 : dtype == 3 ? 8 : 2; }
 
-/* Element idx of a dtype-typed array, as double (exact for both dtypes). */
+/* Element idx of a dtype-typed array, as double (exact for every dtype). */
 static double elem(int dtype, const void *base, int64_t idx) {
     if (dtype == 0) return (double)((const float *)base)[idx];
+    if (dtype == 3) return ((const double *)base)[idx];
     uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
     float f;
     memcpy(&f, &bits, 4);
@@ -69,7 +75,7 @@ static int64_t cache_index(int64_t block, int64_t head, int64_t off, int64_t d,
 int orc_store(int dtype, const void *key, const void *value, void *key_cache, void *value_cache,
               const int32_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
               int32_t block_size, int64_t num_blocks) {
-    if (dtype != 0 && dtype != 1) return fail("bad dtype %d", dtype);
+    if (dtype != 0 && dtype != 1 && dtype != 3) return fail("bad dtype %d", dtype);
     if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
         return fail("bad sizes (tokens %lld, blocks %lld)", (long long)num_tokens, (long long)num_blocks);
     int64_t nslots = num_blocks * block_size;
@@ -95,6 +101,84 @@ int orc_store(int dtype, const void *key, const void *value, void *key_cache, vo
             memcpy((char *)value_cache + dst * eb, (const char *)value + src * eb, (size_t)head_dim * eb);
         }
     }
+    return ORC_OK;
+}
+
+/*
+ * int8 quantization of rows of `dim` elements, one scale per row, all arithmetic in float32:
+ *   a = max_d |x_d|,  scale = a / 127,  code_d = round_half_even(x_d / scale) clamped to [-127, 127];
+ * a row of zeros gets scale 0 and codes 0. Dequantized, x_d ~ code_d * scale, |error| <= scale / 2.
+ * Rows must be finite.
+ */
+int orc_quantize_int8(int dtype, const void *rows, int64_t nrows, int32_t dim, int8_t *codes, float *scales) {
+    if (dtype != 0 && dtype != 1) return fail("bad dtype %d", dtype);
+    if (nrows < 0 || dim <= 0) return fail("bad sizes (rows %lld, dim %d)", (long long)nrows, dim);
+    for (int64_t r = 0; r < nrows; ++r) {
+        float a = 0.0f;
+        for (int32_t d = 0; d < dim; ++d) {
+            float x = (float)elem(dtype, rows, r * dim + d);
+            if (!isfinite(x)) return fail("row %lld holds a non-finite value", (long long)r);
+            if (fabsf(x) > a) a = fabsf(x);
+        }
+        float scale = a / 127.0f;
+        scales[r] = scale;
+        for (int32_t d = 0; d < dim; ++d) {
+            float code = 0.0f;
+            if (a > 0.0f) {
+                float x = (float)elem(dtype, rows, r * dim + d);
+                code = nearbyintf(x / scale);
+                if (code > 127.0f) code = 127.0f;
+                if (code < -127.0f) code = -127.0f;
+            }
+            codes[r * dim + d] = (int8_t)code;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Store into an int8 cache: row (n, h) of key/value is quantized (orc_quantize_int8) and lands at slot
+ * slot_mapping[n] exactly as in orc_store, its scale at the same (block, kv head, offset) of the scale
+ * arrays. Negative slots are skipped; out-of-pool or repeated slots fail before anything is written. */
+int orc_store_int8(int dtype, const void *key, const void *value, int8_t *key_cache, int8_t *value_cache,
+                   float *key_scale, float *value_scale, const int32_t *slot_mapping, int64_t num_tokens,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks) {
+    if (dtype != 0 && dtype != 1) return fail("bad dtype %d", dtype);
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
+        return fail("bad sizes (tokens %lld, blocks %lld)", (long long)num_tokens, (long long)num_blocks);
+    int64_t nslots = num_blocks * block_size;
+    unsigned char *seen = (unsigned char *)calloc((size_t)(nslots > 0 ? nslots : 1), 1);
+    if (!seen) return fail("out of memory");
+    for (int64_t n = 0; n < num_tokens; ++n) {
+        int64_t s = slot_mapping[n];
+        if (s < 0) continue;
+        if (s >= nslots) { free(seen); return fail("slot %lld outside the pool of %lld slots", (long long)s, (long long)nslots); }
+        if (seen[s]) { free(seen); return fail("slot %lld written twice (token %lld)", (long long)s, (long long)n); }
+        seen[s] = 1;
+    }
+    free(seen);
+    size_t eb = elem_bytes(dtype);
+    for (int64_t n = 0; n < num_tokens; ++n) {
+        int64_t s = slot_mapping[n];
+        if (s < 0) continue;
+        int64_t block = s / block_size, off = s % block_size;
+        for (int64_t h = 0; h < num_kv_heads; ++h) {
+            int64_t row = (block * num_kv_heads + h) * block_size + off;
+            int64_t src = (n * num_kv_heads + h) * head_dim;
+            int rc = orc_quantize_int8(dtype, (const char *)key + src * eb, 1, head_dim, key_cache + row * head_dim,
+                                       key_scale + row);
+            if (!rc) rc = orc_quantize_int8(dtype, (const char *)value + src * eb, 1, head_dim,
+                                            value_cache + row * head_dim, value_scale + row);
+            if (rc) return rc;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Dequantize int8 rows: out[r][d] = codes[r][d] * scales[r] in float64 (exact). */
+int orc_dequantize_int8(const int8_t *codes, const float *scales, int64_t nrows, int32_t dim, double *out) {
+    if (nrows < 0 || dim <= 0) return fail("bad sizes (rows %lld, dim %d)", (long long)nrows, dim);
+    for (int64_t r = 0; r < nrows; ++r)
+        for (int32_t d = 0; d < dim; ++d) out[r * dim + d] = (double)codes[r * dim + d] * (double)scales[r];
     return ORC_OK;
 }
 

@@ -12,7 +12,10 @@ What pins what:
   indexing from a pool laid out as ``[num_blocks, num_kv_heads, block_size, head_dim]``, with an
   explicit bottom-right causal mask for chunked prefill;
 * invariants: permuting physical block ids, GQA versus MHA with repeated KV heads, decode versus the
-  last row of causal prefill, chunk-split invariance.
+  last row of causal prefill, chunk-split invariance;
+* int8 cache quantization: exact cases (power-of-two scales), round-half-even ties, the half-step error
+  bound, sign symmetry, placement by slot, and decode on an exactly quantized cache equal to decode on
+  the float cache.
 """
 from __future__ import annotations
 
@@ -281,6 +284,88 @@ def check_gather_matches_numpy_indexing(orc, seed=42):
     assert np.array_equal(vo.astype(np.float64), numpy_gather(vc, bt[0], 14))
 
 
+def check_int8_power_of_two_scale(orc):
+    """Rows whose largest magnitude is 127 * 2^-3 (a negative element) and whose other elements are integer
+    multiples of 2^-3: scale = 2^-3 exactly, codes = the integers, dequantized values = the inputs."""
+    k = np.array([[-127, 5, 0, 126, -3, 64, 1, -1], [100, -127, 7, 0, 0, 0, 2, 9]], np.int64)
+    x = (k * 0.125).astype(np.float32)
+    codes, scales = orc.quantize_int8(F32, x)
+    assert np.array_equal(scales, np.full(2, 0.125, np.float32))
+    assert np.array_equal(codes.astype(np.int64), k)
+    assert np.array_equal(orc.dequantize_int8(codes, scales), x.astype(np.float64))
+
+
+def check_int8_ties_to_even(orc):
+    """scale 1 (absmax 127): halves round to the even integer (round-half-even), both signs."""
+    x = np.array([[127.0, 0.5, 1.5, 2.5, 3.5, -0.5, -2.5, 126.5, -3.5, 0.0]], np.float32)
+    codes, scales = orc.quantize_int8(F32, x)
+    assert scales[0] == 1.0
+    assert codes[0].tolist() == [127, 0, 2, 2, 4, 0, -2, 126, -4, 0]
+
+
+def check_int8_zero_row_bound_and_symmetry(orc, seed=51):
+    """A zero row gives scale 0 and codes 0. Random rows: |code * scale - x| <= scale / 2, the largest
+    magnitude maps to +-127, and negating a row negates its codes with the same scale."""
+    rng = np.random.default_rng(seed)
+    z_codes, z_scales = orc.quantize_int8(F32, np.zeros((1, 16), np.float32))
+    assert z_scales[0] == 0.0 and not z_codes.any()
+    x = (rng.standard_normal((40, 64)) * rng.uniform(0.01, 100, (40, 1))).astype(np.float32)
+    codes, scales = orc.quantize_int8(F32, x)
+    err = np.abs(orc.dequantize_int8(codes, scales) - x.astype(np.float64))
+    assert np.all(err <= scales[:, None].astype(np.float64) * (0.5 + 1e-6))
+    i = np.argmax(np.abs(x), axis=1)
+    assert np.array_equal(np.abs(codes[np.arange(40), i]).astype(np.int64), np.full(40, 127))
+    n_codes, n_scales = orc.quantize_int8(F32, -x)
+    assert np.array_equal(n_scales, scales) and np.array_equal(n_codes.astype(np.int64), -codes.astype(np.int64))
+
+
+def check_int8_store_places_rows(orc, seed=52):
+    """store_int8 puts each row's codes and scale at (s // bs, head, s % bs) of the [NB, Hkv, bs(, D)]
+    arrays; untouched rows keep their sentinels; negative slots write nothing."""
+    rng = np.random.default_rng(seed)
+    nb, hkv, bs, d = 5, 2, 4, 8
+    kc = np.full((nb, hkv, bs, d), 99, np.int8)
+    vc = np.full((nb, hkv, bs, d), -99, np.int8)
+    ks = np.full((nb, hkv, bs), -1.0, np.float32)
+    vs = np.full((nb, hkv, bs), -2.0, np.float32)
+    slots = np.array([3, 17, -1, 8, 19], np.int32)
+    key = rng.standard_normal((5, hkv, d)).astype(np.float32)
+    val = (3 * rng.standard_normal((5, hkv, d))).astype(np.float32)
+    orc.store_int8(F32, key, val, kc, vc, ks, vs, slots)
+    touched = np.zeros((nb, bs), bool)
+    for n, s in enumerate(slots):
+        if s < 0:
+            continue
+        for h in range(hkv):
+            kq, ksc = orc.quantize_int8(F32, key[n, h][None])
+            vq, vsc = orc.quantize_int8(F32, val[n, h][None])
+            assert np.array_equal(kc[s // bs, h, s % bs], kq[0]) and ks[s // bs, h, s % bs] == ksc[0]
+            assert np.array_equal(vc[s // bs, h, s % bs], vq[0]) and vs[s // bs, h, s % bs] == vsc[0]
+        touched[s // bs, s % bs] = True
+    assert np.all(kc.transpose(0, 2, 1, 3)[~touched] == 99) and np.all(vc.transpose(0, 2, 1, 3)[~touched] == -99)
+    assert np.all(ks.transpose(0, 2, 1)[~touched] == -1.0) and np.all(vs.transpose(0, 2, 1)[~touched] == -2.0)
+
+
+def check_int8_decode_exact_case_matches_float_decode(orc, seed=53):
+    """When every row is an integer multiple of a power of two with absmax 127 times it, quantization
+    is exact, so decode over the dequantized int8 cache ("f64") equals decode over the float cache."""
+    rng = np.random.default_rng(seed)
+    nb, hkv, bs, d = 8, 2, 4, 8
+    ints = rng.integers(-127, 128, size=(nb, hkv, bs, d))
+    ints[..., 0] = np.where(rng.random((nb, hkv, bs)) < 0.5, 127, -127)
+    kf = (ints * 0.25).astype(np.float32)
+    vf = (np.roll(ints, 1, axis=-1) * 0.5).astype(np.float32)
+    kq, ks = orc.quantize_int8(F32, kf)
+    vq, vs = orc.quantize_int8(F32, vf)
+    bt = _tables(rng, [13, 5], bs, nb)
+    q = rng.standard_normal((2, 4, d)).astype(np.float32)
+    lens = np.array([13, 5], np.int32)
+    ref = orc.decode(F32, q, kf, vf, bt, lens, 0.01)
+    got = orc.decode("f64", q.astype(np.float64), orc.dequantize_int8(kq, ks), orc.dequantize_int8(vq, vs), bt, lens,
+                     0.01)
+    assert np.abs(got - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
 ALL_CHECKS = [
     check_gather_matches_numpy_indexing,
     check_single_key,
@@ -295,4 +380,9 @@ ALL_CHECKS = [
     check_decode_is_last_prefill_row,
     check_chunk_split_invariance,
     check_store_places_rows,
+    check_int8_power_of_two_scale,
+    check_int8_ties_to_even,
+    check_int8_zero_row_bound_and_symmetry,
+    check_int8_store_places_rows,
+    check_int8_decode_exact_case_matches_float_decode,
 ]

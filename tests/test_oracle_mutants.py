@@ -59,6 +59,12 @@ MUTANTS = {
     "gather_reads_wrong_head": ("int64_t src = cache_index(block, h, off, 0, num_kv_heads, block_size, head_dim);",
                                 "int64_t src = cache_index(block, 0, off, 0, num_kv_heads, block_size, head_dim);"),
     "prefill_row_owner_off_by_one": ("while (cu_seqlens_q[i + 1] <= r) ++i;", "while (cu_seqlens_q[i + 1] < r) ++i;"),
+    "int8_truncates": ("code = nearbyintf(x / scale);", "code = truncf(x / scale);"),
+    "int8_scale_over_128": ("float scale = a / 127.0f;", "float scale = a / 128.0f;"),
+    "int8_signed_max": ("if (fabsf(x) > a) a = fabsf(x);", "if (x > a) a = x;"),
+    "int8_dequant_drops_scale": ("(double)codes[r * dim + d] * (double)scales[r];", "(double)codes[r * dim + d];"),
+    "int8_store_scale_at_offset": ("key_cache + row * head_dim,\n                                       key_scale + row);",
+                                   "key_cache + row * head_dim,\n                                       key_scale + off);"),
 }
 
 
