@@ -6,7 +6,9 @@
  *   pkv_paged_attention_decode  one query token per sequence attends over its cached tokens;
  *   pkv_paged_attention_prefill a varlen chunk of queries per sequence attends causally over its
  *                               cached prefix plus the chunk;
- *   pkv_kv_cache_gather         inverse of the store for one block table (test helper).
+ *   pkv_kv_cache_gather         inverse of the store for one block table (test helper);
+ *   pkv_kv_cache_copy_blocks    copy whole blocks (copy-on-write of shared blocks);
+ *   pkv_kv_cache_store_int8, pkv_paged_attention_decode_int8: the same over an int8 cache.
  *
  * Vocabulary (nano-vllm walkthrough, section 2 context: is_prefill, cu_seqlens_q/k, max_seqlen_q/k,
  * slot_mapping, context_lens, block_tables; "推理运行时", section 分页 KV: logical block j of a
@@ -158,6 +160,44 @@ pkv_status pkv_kv_cache_gather(pkv_dtype dtype, void *key_out, void *value_out, 
 pkv_status pkv_kv_cache_copy_blocks(pkv_dtype dtype, void *key_cache, void *value_cache, const int32_t *pairs,
                                     int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                     int64_t num_blocks, hipStream_t stream);
+
+/*
+ * int8 KV cache ("LLM Infra 101 v0.2: KV Cache", inference-engine list, KV Quantization: the cache keeps
+ * K/V as int8 instead of bf16, trading some accuracy for half the bytes). The pages fix no scheme; this
+ * library keeps one fp32 scale per (token, kv head) row:
+ *   scale = max_d |x_d| / 127,  code_d = round_half_even(x_d / scale) clamped to [-127, 127]
+ * computed in fp32 with IEEE division (a row of zeros: scale 0, codes 0), so codes are bit-exact with
+ * any implementation of the same formula. Dequantized, x_d ~ code_d * scale with |error| <= scale / 2.
+ *   key_cache, value_cache  int8 [num_blocks][num_kv_heads][block_size][head_dim];
+ *   key_scale, value_scale  fp32 [num_blocks][num_kv_heads][block_size], one per cache row.
+ */
+
+/*
+ * kv_cache_store_int8: like pkv_kv_cache_store, but each (token, kv head) row of key / value (dtype
+ * PKV_F32 or PKV_BF16, [num_tokens][num_kv_heads][head_dim], head_dim 64 or 128) is quantized as above;
+ * its codes land in the int8 caches at the slot's row and its scale at the same (block, kv head, offset)
+ * of the scale arrays. Rows must be finite. Cache pointers 16-byte aligned, scales 4-byte aligned.
+ */
+pkv_status pkv_kv_cache_store_int8(pkv_dtype dtype, const void *key, const void *value, int8_t *key_cache,
+                                   int8_t *value_cache, float *key_scale, float *value_scale,
+                                   const int32_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int64_t num_blocks, hipStream_t stream);
+
+/*
+ * paged_attention_decode_int8: pkv_paged_attention_decode over an int8 cache: attention over the
+ * dequantized K/V (code * scale). dtype (query and out) must be PKV_BF16, head_dim 128, block_size >= 16
+ * (PKV_EUNSUPPORTED otherwise). q.k runs on MFMA with the codes as exact bf16 integers and fp32
+ * accumulation, times the row's K scale; each softmax weight is multiplied by its row's V scale and
+ * rounded to bf16 for p.v (the denominator sums the unrounded weights). Scale arrays 16-byte aligned.
+ * Workspace: pkv_paged_attention_decode_workspace_size with the same sizes.
+ */
+pkv_status pkv_paged_attention_decode_int8(pkv_dtype dtype, void *out, const void *query, const int8_t *key_cache,
+                                           const int8_t *value_cache, const float *key_scale,
+                                           const float *value_scale, const int32_t *block_tables,
+                                           int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
+                                           int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                           void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Message of the calling thread's last non-OK status ("" if none). Owned by the library. */
 const char *pkv_last_error(void);

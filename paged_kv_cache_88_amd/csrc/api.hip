@@ -198,12 +198,16 @@ size_t pkv_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_h
     return plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len).ws_bytes;
 }
 
-pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *query, const void *key_cache,
-                                      const void *value_cache, const int32_t *block_tables,
-                                      int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
-                                      int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
-                                      int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
-                                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and argument set-up shared by the decode entry points (cache element bytes: 4, 2 or 1).
+pkv_status decode_args(pkv::DecodeArgs &a, pkv_dtype dtype, int cache_elem_bytes, void *out, const void *query,
+                       const void *key_cache, const void *value_cache, const int32_t *block_tables,
+                       int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
+                       int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int64_t num_blocks, float scale, void *workspace, size_t workspace_bytes) {
     pkv_status st = check_common(dtype, num_kv_heads, head_dim, block_size, num_blocks);
     if (st != PKV_OK) return st;
     st = check_heads(num_heads, num_kv_heads);
@@ -221,6 +225,7 @@ pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *qu
     REQUIRE(block_tables || max_context_len == 0, PKV_EINVAL, "null block_tables");
     REQUIRE(aligned16(out) && aligned16(query) && aligned16(key_cache) && aligned16(value_cache), PKV_EINVAL,
             "out, query and cache pointers must be 16-byte aligned");
+    (void)cache_elem_bytes;
     DecodePlan plan = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len);
     REQUIRE((int64_t)num_seqs * (((int64_t)max_context_len + 31) / 32) < ((int64_t)1 << 30), PKV_EINVAL,
             "num_seqs * max_context_len too large (at most 2^35 tokens)");
@@ -229,7 +234,7 @@ pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *qu
     REQUIRE(workspace != nullptr && workspace_bytes >= plan.ws_bytes, PKV_EWORKSPACE,
             "decode needs %zu bytes of workspace (got %zu)", plan.ws_bytes, workspace_bytes);
     REQUIRE(((uintptr_t)workspace & 255u) == 0, PKV_EINVAL, "workspace must be 256-byte aligned");
-    pkv::DecodeArgs a{};
+    a = pkv::DecodeArgs{};
     a.out = out;
     a.query = query;
     a.key_cache = key_cache;
@@ -254,8 +259,69 @@ pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *qu
     a.ws_m = (float *)((char *)workspace + plan.off_m);
     a.ws_l = (float *)((char *)workspace + plan.off_l);
     a.ws_o = (float *)((char *)workspace + plan.off_o);
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *query, const void *key_cache,
+                                      const void *value_cache, const int32_t *block_tables,
+                                      int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
+                                      int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    pkv::DecodeArgs a;
+    pkv_status st = decode_args(a, dtype, elem_bytes(dtype), out, query, key_cache, value_cache, block_tables,
+                                block_table_stride, context_lens, num_seqs, max_context_len, num_heads, num_kv_heads,
+                                head_dim, block_size, num_blocks, scale, workspace, workspace_bytes);
+    if (st != PKV_OK || num_seqs == 0) return st;
     return hip_status(pkv::launch_decode(a, dtype == PKV_BF16, head_dim, num_heads / num_kv_heads, stream),
                       "paged_attention_decode launch");
+}
+
+pkv_status pkv_kv_cache_store_int8(pkv_dtype dtype, const void *key, const void *value, int8_t *key_cache,
+                                   int8_t *value_cache, float *key_scale, float *value_scale,
+                                   const int32_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int64_t num_blocks, hipStream_t stream) {
+    pkv_status st = check_common(dtype, num_kv_heads, head_dim, block_size, num_blocks);
+    if (st != PKV_OK) return st;
+    REQUIRE(num_tokens >= 0, PKV_EINVAL, "num_tokens must be non-negative (got %lld)", (long long)num_tokens);
+    if (num_tokens == 0) return ok();
+    REQUIRE(key && value && key_cache && value_cache && key_scale && value_scale && slot_mapping, PKV_EINVAL,
+            "null pointer argument");
+    REQUIRE(aligned16(key) && aligned16(value) && aligned16(key_cache) && aligned16(value_cache) &&
+                ((uintptr_t)key_scale & 3u) == 0 && ((uintptr_t)value_scale & 3u) == 0,
+            PKV_EINVAL, "key, value and cache pointers must be 16-byte aligned, scales 4-byte aligned");
+    REQUIRE(num_tokens * num_kv_heads <= (int64_t)1 << 40, PKV_EINVAL, "num_tokens too large");
+    return hip_status(pkv::launch_store_int8(dtype == PKV_BF16, head_dim, key, value, key_cache, value_cache, key_scale,
+                                             value_scale, slot_mapping, num_tokens, num_kv_heads, block_size,
+                                             (int)num_blocks, stream),
+                      "kv_cache_store_int8 launch");
+}
+
+pkv_status pkv_paged_attention_decode_int8(pkv_dtype dtype, void *out, const void *query, const int8_t *key_cache,
+                                           const int8_t *value_cache, const float *key_scale,
+                                           const float *value_scale, const int32_t *block_tables,
+                                           int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
+                                           int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    REQUIRE(dtype == PKV_BF16, PKV_EUNSUPPORTED, "int8-cache decode takes a bf16 query (got dtype %d)", (int)dtype);
+    REQUIRE(head_dim == 128, PKV_EUNSUPPORTED, "int8-cache decode supports head_dim 128 (got %d)", head_dim);
+    REQUIRE(block_size >= 16, PKV_EUNSUPPORTED, "int8-cache decode needs block_size >= 16 (got %d)", block_size);
+    pkv::DecodeArgs a;
+    pkv_status st = decode_args(a, dtype, 1, out, query, key_cache, value_cache, block_tables, block_table_stride,
+                                context_lens, num_seqs, max_context_len, num_heads, num_kv_heads, head_dim, block_size,
+                                num_blocks, scale, workspace, workspace_bytes);
+    if (st != PKV_OK || num_seqs == 0) return st;
+    REQUIRE(key_scale && value_scale, PKV_EINVAL, "null scale array");
+    REQUIRE(((uintptr_t)key_scale & 15u) == 0 && ((uintptr_t)value_scale & 15u) == 0, PKV_EINVAL,
+            "scale arrays must be 16-byte aligned");
+    a.key_scale = key_scale;
+    a.value_scale = value_scale;
+    return hip_status(pkv::launch_decode_int8(a, num_heads / num_kv_heads, stream), "paged_attention_decode_int8 launch");
 }
 
 pkv_status pkv_paged_attention_prefill(pkv_dtype dtype, void *out, const void *query, const void *key_cache,

@@ -527,10 +527,28 @@ decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x
 // Buffer descriptor word 3 for raw (untyped, unswizzled) buffers on gfx9-family GPUs.
 constexpr int BUF_RSRC_W3 = 0x00020000;
 
-// 16-byte load through a buffer descriptor; non-temporal unless PKV_DECODE_NT is 0.
+// 16- and 8-byte loads through a buffer descriptor; non-temporal unless PKV_DECODE_NT is 0.
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, PKV_DECODE_NT ? 2 : 0);
 }
+__device__ __forceinline__ u32x2 buffer_load8(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, PKV_DECODE_NT ? 2 : 0);
+}
+
+// Registers of one 32-token tile of the matrix-core decode: bf16 rows, or int8 codes plus per-row scales.
+template <bool Q8>
+struct MfmaTile {
+    u32x4 k[2][4];
+    u32x4 v[2][4];
+    bool live[2];                           // group's block id lies in the pool
+};
+template <>
+struct MfmaTile<true> {
+    u32x4 k[2][2];                          // per group: dims 16 b .. +16 and 64 + 16 b .. +16 of row n
+    u32x2 v[2][4];                          // per group and i: dims 8 n .. +8 of row 4 b + i
+    f32x4 ks[2], vs[2];                     // scales of rows 4 b .. 4 b + 3 of each group
+    bool live[2];
+};
 
 // The same units on the matrix cores (bf16, head_dim 128, block_size >= 16), with a persistent grid:
 // one workgroup of one wave per resident wave slot, each taking units from the list until it is done.
@@ -555,15 +573,23 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byt
 // during the current unit), so a wave pays the dependent-load chain of a unit start only once.
 // Block size >= 16 puts each 16-token group in one block: the block id and block base are wave-uniform
 // and lanes add 32-bit row offsets.
-template <int G>
+//
+// int8 caches (Q8): rows hold int8 codes with one fp32 scale per (token, kv head). K codes of a lane are
+// two 16-byte loads (dims 16 b .. +16 and 64 + 16 b .. +16, the MFMA reduction order permuted to match,
+// Q loaded in the same order), V codes one 8-byte load per token; codes become exact bf16 integers in
+// registers, the K scale multiplies each score, and the V scale multiplies each weight before it is
+// rounded to bf16 (the denominator sums the unscaled weights).
+template <int G, bool Q8>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x4 *__restrict__ key_cache,
-                   const u32x4 *__restrict__ value_cache, const int32_t *__restrict__ block_tables, int bt_stride,
+decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const char *__restrict__ key_cache,
+                   const char *__restrict__ value_cache, const int32_t *__restrict__ block_tables, int bt_stride,
                    const int4 *__restrict__ items, const int *__restrict__ ctrl, int num_kv_heads,
                    int64_t num_blocks, int log2_bs, float scale_log2e,
-                   float *__restrict__ ws_m, float *__restrict__ ws_l, float *__restrict__ ws_o) {
+                   float *__restrict__ ws_m, float *__restrict__ ws_l, float *__restrict__ ws_o,
+                   const float *__restrict__ key_scale, const float *__restrict__ value_scale) {
     static_assert(G >= 1 && G <= 16, "query heads per kv head");
-    constexpr int D = 128, CH = D / 8;        // 16-byte chunks per row
+    constexpr int D = 128, CH = D / 8;        // 16-byte chunks of a bf16 row
+    constexpr int RB = Q8 ? D : 2 * D;        // bytes per cache row
     constexpr int TILE = 32;
     const int lane = threadIdx.x, n = lane & 15, b = lane >> 4;
     const int num_heads = num_kv_heads * G;
@@ -603,19 +629,18 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
         const u32x4 *qv = (const u32x4 *)query;
         const int64_t row = ((int64_t)x.seq * num_heads + x.kvh * G + (n < G ? n : 0)) * CH;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) qt[c] = n < G ? qv[row + 4 * c + b] : u32x4{0, 0, 0, 0};
+        for (int c = 0; c < 4; ++c) {
+            const int chunk = Q8 ? (c < 2 ? 2 * b + c : 8 + 2 * b + (c - 2)) : 4 * c + b;
+            qt[c] = n < G ? qv[row + chunk] : u32x4{0, 0, 0, 0};
+        }
     };
 
-    struct Tile {
-        u32x4 k[2][4];
-        u32x4 v[2][4];
-        bool live[2];                           // group holds at least one token and a valid block id
-    };
+    using Tile = MfmaTile<Q8>;
     // Rows past the unit's end are clamped to its last token (same block: a group past the end is
     // clamped whole), so every lane reads a row holding finite data; such tokens get zero weight.
     // Loads go through buffer descriptors of the group's (block, kv head) slab: wave-uniform base,
     // 32-bit lane offsets, and the hardware range check bounds every access to the slab.
-    const uint32_t slab_bytes = (uint32_t)CH * 16u << log2_bs;
+    const uint32_t slab_bytes = (uint32_t)RB << log2_bs;
     auto issue = [&](const Unit &x, int xblk, int tile, Tile &t) {
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
@@ -624,18 +649,34 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
             const int tokc = x.start + tlc;
             const int64_t blk = __builtin_amdgcn_readlane(xblk, (tokc >> log2_bs) - x.first_blk);
             t.live[g] = blk >= 0 && blk < num_blocks;
-            const int64_t slab = t.live[g] ? ((blk * num_kv_heads + x.kvh) << log2_bs) * CH : 0;
-            const __amdgpu_buffer_rsrc_t kr =
-                __builtin_amdgcn_make_buffer_rsrc((void *)(key_cache + slab), (short)0, (int)slab_bytes, BUF_RSRC_W3);
-            const __amdgpu_buffer_rsrc_t vr =
-                __builtin_amdgcn_make_buffer_rsrc((void *)(value_cache + slab), (short)0, (int)slab_bytes, BUF_RSRC_W3);
+            const int64_t slab = t.live[g] ? ((blk * num_kv_heads + x.kvh) << log2_bs) : 0;   // first row
+            const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(key_cache + slab * RB), (short)0, (int)slab_bytes, BUF_RSRC_W3);
+            const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(value_cache + slab * RB), (short)0, (int)slab_bytes, BUF_RSRC_W3);
             const int last = x.ntok - 1 - tl0;              // rows past it are clamped to it
             const int r0 = (tokc & bs_mask) - tlc + tl0;    // slab row of token tl0
-            const int koff = ((r0 + min(n, last)) * CH + b) * 16;
+            if constexpr (Q8) {
+                const int koff = (r0 + min(n, last)) * RB + 16 * b;
+                t.k[g][0] = buffer_load16(kr, koff);
+                t.k[g][1] = buffer_load16(kr, koff + 64);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) t.k[g][c] = buffer_load16(kr, koff + 64 * c);
+                for (int i = 0; i < 4; ++i) t.v[g][i] = buffer_load8(vr, (r0 + min(4 * b + i, last)) * RB + 8 * n);
+                // scales of the 16-row group holding the clamped token (its own rows when the group is live)
+                const int srow = (tokc & bs_mask) & ~15;
+                const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(key_scale + slab), (short)0, 4 << log2_bs, BUF_RSRC_W3);
+                const __amdgpu_buffer_rsrc_t vsr = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(value_scale + slab), (short)0, 4 << log2_bs, BUF_RSRC_W3);
+                t.ks[g] = __builtin_bit_cast(f32x4, buffer_load16(ksr, (srow + 4 * b) * 4));
+                t.vs[g] = __builtin_bit_cast(f32x4, buffer_load16(vsr, (srow + 4 * b) * 4));
+            } else {
+                const int koff = (r0 + min(n, last)) * RB + 16 * b;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) t.v[g][i] = buffer_load16(vr, ((r0 + min(4 * b + i, last)) * CH + n) * 16);
+                for (int c = 0; c < 4; ++c) t.k[g][c] = buffer_load16(kr, koff + 64 * c);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t.v[g][i] = buffer_load16(vr, (r0 + min(4 * b + i, last)) * RB + 16 * n);
+            }
         }
     };
 
@@ -648,28 +689,57 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
         // masked tokens: past the unit's end (only in its last tile), or in a block outside the pool,
         // whose rows (block 0) may hold anything: those get V zeroed as well
         const bool partial = (tile + 1) * TILE > x.ntok || !t.live[0] || !t.live[1];   // wave-uniform
+        // bf16 operands of the tile (int8 codes are converted exactly)
+        u32x4 tk[2][4], tv[2][4];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            if constexpr (Q8) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const u32x4 w = t.k[g][c >> 1];
+                    const uint32_t w0 = (c & 1) ? w[2] : w[0], w1 = (c & 1) ? w[3] : w[1];
+                    tk[g][c] = u32x4{i8pair_to_bf16x2(w0, 0), i8pair_to_bf16x2(w0, 1), i8pair_to_bf16x2(w1, 0),
+                                     i8pair_to_bf16x2(w1, 1)};
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    tv[g][i] = u32x4{i8pair_to_bf16x2(t.v[g][i][0], 0), i8pair_to_bf16x2(t.v[g][i][0], 1),
+                                     i8pair_to_bf16x2(t.v[g][i][1], 0), i8pair_to_bf16x2(t.v[g][i][1], 1)};
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) tk[g][c] = t.k[g][c];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tv[g][i] = t.v[g][i];
+            }
+        }
         if (!t.live[0] || !t.live[1]) {
 #pragma unroll
             for (int g = 0; g < 2; ++g)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (!t.live[g]) t.v[g][i] = u32x4{0, 0, 0, 0};
+                    if (!t.live[g]) tv[g][i] = u32x4{0, 0, 0, 0};
         }
         f32x4 s[2];
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             s[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < 4; ++c) s[g] = mfma16x16x32(t.k[g][c], qt[c], s[g]);
+            for (int c = 0; c < 4; ++c) s[g] = mfma16x16x32(tk[g][c], qt[c], s[g]);
         }
-        float xs[2][4];
+        float xs[2][4], vsc[2][4];
         float mx = -INFINITY;
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool ok = !partial || (t.live[g] && tile * TILE + 16 * g + 4 * b + i < x.ntok);
-                xs[g][i] = ok ? s[g][i] * scale_log2e : -INFINITY;
+                float sc = scale_log2e;
+                vsc[g][i] = 1.f;
+                if constexpr (Q8) {
+                    sc *= t.ks[g][i];
+                    vsc[g][i] = ok ? t.vs[g][i] : 0.f;
+                }
+                xs[g][i] = ok ? s[g][i] * sc : -INFINITY;
                 mx = fmaxf(mx, xs[g][i]);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -684,27 +754,38 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
         }
         constexpr uint32_t ONES = 0x3f803f80u;
         u32x4 pb;
+        if constexpr (Q8) {
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            pb[2 * g] = pack_bf16x2(fast_exp2(xs[g][0] - m), fast_exp2(xs[g][1] - m));
-            pb[2 * g + 1] = pack_bf16x2(fast_exp2(xs[g][2] - m), fast_exp2(xs[g][3] - m));
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const float p0 = fast_exp2(xs[g][2 * h2] - m), p1 = fast_exp2(xs[g][2 * h2 + 1] - m);
+                    l += p0 + p1;
+                    pb[2 * g + h2] = pack_bf16x2(p0 * vsc[g][2 * h2], p1 * vsc[g][2 * h2 + 1]);
+                }
+        } else {
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                pb[2 * g] = pack_bf16x2(fast_exp2(xs[g][0] - m), fast_exp2(xs[g][1] - m));
+                pb[2 * g + 1] = pack_bf16x2(fast_exp2(xs[g][2] - m), fast_exp2(xs[g][3] - m));
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w) l = dot2_bf16(pb[w], ONES, l);
         }
-#pragma unroll
-        for (int w = 0; w < 4; ++w) l = dot2_bf16(pb[w], ONES, l);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int w = j >> 1;
             u32x4 a;
             if (j & 1) {
-                a[0] = pair_hi(t.v[0][0][w], t.v[0][1][w]);
-                a[1] = pair_hi(t.v[0][2][w], t.v[0][3][w]);
-                a[2] = pair_hi(t.v[1][0][w], t.v[1][1][w]);
-                a[3] = pair_hi(t.v[1][2][w], t.v[1][3][w]);
+                a[0] = pair_hi(tv[0][0][w], tv[0][1][w]);
+                a[1] = pair_hi(tv[0][2][w], tv[0][3][w]);
+                a[2] = pair_hi(tv[1][0][w], tv[1][1][w]);
+                a[3] = pair_hi(tv[1][2][w], tv[1][3][w]);
             } else {
-                a[0] = pair_lo(t.v[0][0][w], t.v[0][1][w]);
-                a[1] = pair_lo(t.v[0][2][w], t.v[0][3][w]);
-                a[2] = pair_lo(t.v[1][0][w], t.v[1][1][w]);
-                a[3] = pair_lo(t.v[1][2][w], t.v[1][3][w]);
+                a[0] = pair_lo(tv[0][0][w], tv[0][1][w]);
+                a[1] = pair_lo(tv[0][2][w], tv[0][3][w]);
+                a[2] = pair_lo(tv[1][0][w], tv[1][1][w]);
+                a[3] = pair_lo(tv[1][2][w], tv[1][3][w]);
             }
             acc[j] = mfma16x16x32(a, pb, acc[j]);
         }
@@ -862,10 +943,11 @@ static hipError_t launch_decode_cfg(const DecodeArgs &a, hipStream_t stream) {
     if constexpr (MFMA) {
         static_assert(BF16 && D == 128, "matrix-core decode: bf16, head_dim 128");
         const int64_t grid = units < a.workers ? units : a.workers;
-        hipLaunchKernelGGL((decode_mfma_kernel<G>), dim3((unsigned)grid), dim3(64), 0, stream, a.out, a.query,
-                           (const u32x4 *)a.key_cache, (const u32x4 *)a.value_cache, a.block_tables, a.bt_stride,
-                           a.items, a.ctrl, a.num_kv_heads, a.num_blocks, a.log2_bs, a.scale_log2e, a.ws_m, a.ws_l,
-                           a.ws_o);
+        const bool q8 = a.key_scale != nullptr;
+        hipLaunchKernelGGL((q8 ? decode_mfma_kernel<G, true> : decode_mfma_kernel<G, false>), dim3((unsigned)grid),
+                           dim3(64), 0, stream, a.out, a.query, (const char *)a.key_cache, (const char *)a.value_cache,
+                           a.block_tables, a.bt_stride, a.items, a.ctrl, a.num_kv_heads, a.num_blocks, a.log2_bs,
+                           a.scale_log2e, a.ws_m, a.ws_l, a.ws_o, a.key_scale, a.value_scale);
     } else {
         hipLaunchKernelGGL((decode_kernel<BF16, D, G, NV, R, NW>), dim3((unsigned)units), dim3(64 * NW), 0, stream,
                            a.out, a.query, (const u32x4 *)a.key_cache, (const u32x4 *)a.value_cache, a.block_tables,
@@ -925,6 +1007,22 @@ hipError_t launch_decode(const DecodeArgs &a, bool bf16, int head_dim, int group
                                      : launch_decode_d<true, 64>(a, group, stream);
     return head_dim == 128 ? launch_decode_d<false, 128>(a, group, stream)
                            : launch_decode_d<false, 64>(a, group, stream);
+}
+
+hipError_t launch_decode_int8(const DecodeArgs &a, int group, hipStream_t stream) {
+    if (a.num_seqs == 0) return hipSuccess;
+    if (a.log2_bs < 4 || a.key_scale == nullptr || a.value_scale == nullptr) return hipErrorInvalidValue;
+    switch (group) {
+        case 1: return launch_decode_cfg<true, 128, 1, 2, 2, 1, true>(a, stream);
+        case 2: return launch_decode_cfg<true, 128, 2, 2, 2, 1, true>(a, stream);
+        case 3: return launch_decode_cfg<true, 128, 3, 2, 2, 1, true>(a, stream);
+        case 4: return launch_decode_cfg<true, 128, 4, 2, 2, 1, true>(a, stream);
+        case 5: return launch_decode_cfg<true, 128, 5, 1, 4, 1, true>(a, stream);
+        case 6: return launch_decode_cfg<true, 128, 6, 1, 4, 1, true>(a, stream);
+        case 7: return launch_decode_cfg<true, 128, 7, 1, 4, 1, true>(a, stream);
+        case 8: return launch_decode_cfg<true, 128, 8, 1, 4, 1, true>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 int decode_max_part_blocks() { return MAX_PART_BLOCKS; }

@@ -15,6 +15,7 @@ __device__ __forceinline__ int64_t cache_row(int64_t block, int kvh, int off, in
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -86,6 +87,21 @@ __device__ __forceinline__ void group_sum_all(float *v) {
 #pragma unroll
         for (int k = 0; k < K; ++k) v[k] += dpp<DPP_MIRROR>(v[k]);
     }
+}
+
+// Max over an aligned group of N lanes (N in {1, 2, 4, 8, 16}), same butterfly as group_sum.
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+    if constexpr (N >= 2) v = fmaxf(v, dpp<DPP_XOR1>(v));
+    if constexpr (N >= 4) v = fmaxf(v, dpp<DPP_XOR2>(v));
+    if constexpr (N >= 8) v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+    if constexpr (N >= 16) v = fmaxf(v, dpp<DPP_MIRROR>(v));
+    return v;
+}
+
+// Bytes 2k and 2k + 1 of w, as signed 8-bit integers, to a bf16 pair (exact: |code| <= 128).
+__device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t w, int k) {
+    return pack_bf16x2((float)(int8_t)(w >> (16 * k)), (float)(int8_t)(w >> (16 * k + 8)));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -38,7 +38,6 @@
 
 namespace pkv {
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int PF_THREADS = 256;
 constexpr int PF_D = 128;

@@ -130,3 +130,24 @@ def test_binding_fails_loudly_without_library(pkv, tmp_path):
             pkv.load_library(str(tmp_path / "nope.so"))
     finally:
         pkv._lib = saved
+
+
+def test_int8_entry_points_validation(lib):
+    """int8 cache calls: unsupported shapes and missing scales are refused before any launch."""
+    store = lib.pkv_kv_cache_store_int8
+    # head_dim 96 unsupported; null scale; misaligned scale; zero tokens is a no-op
+    assert store(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 96, 16, 8, None) == 2
+    assert store(1, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 2, 128, 16, 8, None) == 1
+    assert store(1, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 2), FAKE, FAKE, 4, 2, 128, 16, 8, None) == 1
+    assert store(1, None, None, None, None, None, None, None, 0, 2, 128, 16, 8, None) == 0
+    dec = lib.pkv_paged_attention_decode_int8
+    # fp32 query, head_dim 64 and block size 8 have no int8 kernel
+    assert dec(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 10, 8, 2, 128, 16, 64, 0.1, None, 0, None) == 2
+    assert dec(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 10, 8, 2, 64, 16, 64, 0.1, None, 0, None) == 2
+    assert dec(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 10, 8, 2, 128, 8, 64, 0.1, None, 0, None) == 2
+    assert "block_size" in _err(lib)
+    # workspace missing; null scales (with enough workspace) are refused
+    need = lib.pkv_paged_attention_decode_workspace_size(2, 8, 2, 128, 16, 64)
+    assert dec(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 8, 2, 128, 16, 64, 0.1, None, 0, None) == 3
+    assert dec(1, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, FAKE, 2, 64, 8, 2, 128, 16, 64, 0.1,
+               ctypes.c_void_p(1 << 24), need, None) == 1
