@@ -11,7 +11,8 @@ R * step bytes >> the last-level cache), so K/V come from HBM, not from cache.
 
 Prints one JSON line (rank 0): value = algorithmic bytes of the step / step time (GB/s), plus the
 roofline of the decode call measured with HIP events on the launch stream, and the CPU oracle's rate
-on a bounded sample of the same workload.
+on a bounded sample of the same workload. Secondary legs (not part of `value`): the same decode over
+an int8 cache, and the chunked-prefill workload on MFMA.
 """
 from __future__ import annotations
 
@@ -39,6 +40,61 @@ def decode_bytes(c) -> int:
     nb = -(-lens // c.block_size)
     return int(2 * lens.sum() * c.num_kv_heads * c.head_dim * e + 2 * c.num_seqs * c.num_heads * c.head_dim * e
                + 4 * nb.sum() + 4 * c.num_seqs)
+
+
+def decode_bytes_int8(c) -> int:
+    """Algorithmic bytes of one decode call over an int8 cache: the int8 codes of K and V of every context
+    token, their fp32 row scales, q and out (bf16), the block-table entries used and context_lens."""
+    lens = c.context_lens.astype(np.int64)
+    nb = -(-lens // c.block_size)
+    return int(2 * lens.sum() * c.num_kv_heads * (c.head_dim + 4) + 2 * c.num_seqs * c.num_heads * c.head_dim * 2
+               + 4 * nb.sum() + 4 * c.num_seqs)
+
+
+def bench_int8(pkv, torch, W, c, dev, copies, steps, warmup):
+    """The same decode workload over an int8 cache (rows quantized by kv_cache_store_int8 from the bf16
+    values; pool copies rotated as in the main leg): average decode-call time from HIP events."""
+    kr, vr, slots = W.cached_rows(c.pool)
+
+    def tt(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    kr, vr, slots = tt(kr), tt(vr), torch.from_numpy(slots).to(dev)
+    shape = (c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
+    pools = []
+    for _ in range(copies):
+        kc = torch.zeros(shape, dtype=torch.int8, device=dev)
+        vc = torch.zeros_like(kc)
+        ks = torch.zeros(shape[:3], dtype=torch.float32, device=dev)
+        vs = torch.zeros_like(ks)
+        pkv.kv_cache_store_int8(kr, vr, kc, vc, ks, vs, slots)
+        pkv.kv_cache_store_int8(tt(c.key), tt(c.value), kc, vc, ks, vs, torch.from_numpy(c.slot_mapping).to(dev))
+        pools.append((kc, vc, ks, vs))
+    q = tt(c.query)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(c.block_tables).to(dev)
+    cl = torch.from_numpy(c.context_lens).to(dev)
+    ws = torch.empty(pkv.decode_workspace_size(c.num_seqs, c.num_heads, c.num_kv_heads, c.head_dim, c.block_size,
+                                               c.max_context_len), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for k in range(warmup + steps):
+        kc, vc, ks, vs = pools[k % copies]
+        if k >= warmup:
+            ev[k - warmup][0].record(stream)
+        pkv.paged_attention_decode_int8(out, q, kc, vc, ks, vs, bt, cl, c.max_context_len, c.scale, workspace=ws,
+                                        stream=stream)
+        if k >= warmup:
+            ev[k - warmup][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nbytes = decode_bytes_int8(c)
+    return {"workload": c.name, "cache": "int8 codes + fp32 scale per (token, kv head) row",
+            "decode_ms": round(ms, 5), "algorithmic_bytes": nbytes,
+            "achieved_gbs": round(nbytes / (ms * 1e-3) / 1e9, 2),
+            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "decode_tokens_per_s": round(c.num_seqs / (ms * 1e-3), 1),
+            "outputs_finite": bool(torch.isfinite(out.float()).all().item())}
 
 
 def store_bytes(c) -> int:
@@ -168,6 +224,7 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="pool copies rotated per step (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
+    ap.add_argument("--no-int8", action="store_true", help="skip the int8-cache decode leg")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -276,8 +333,12 @@ def main():
         "gpu": torch.cuda.get_device_name(0),
         "torch": torch.__version__,
     }
-    if not args.no_prefill:
+    if c.dtype == "bf16" and c.head_dim == 128 and c.block_size >= 16 and not args.no_int8:
         del pools
+        result["int8_cache"] = bench_int8(pkv, torch, W, c, dev, copies, args.steps, args.warmup)
+        result["int8_cache"]["speedup_vs_bf16_cache"] = round(dec_avg_ms / result["int8_cache"]["decode_ms"], 3)
+    if not args.no_prefill:
+        pools = None
         result["prefill"] = bench_prefill(pkv, torch, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(c)

@@ -29,17 +29,6 @@ def _floats(a, dtype):
     return W.bf16_bits_to_f32(a) if dtype == W.BF16 else np.asarray(a, np.float32)
 
 
-def cached_rows(pool):
-    """Every row of the owned blocks as store input ([N, Hkv, D] K and V, storage dtype) with its slot;
-    rows holding NaN (tokens not cached yet) get slot -1."""
-    u, hkv, bs, d = pool.key_blocks.shape
-    kr = pool.key_blocks.transpose(0, 2, 1, 3).reshape(u * bs, hkv, d)
-    vr = pool.value_blocks.transpose(0, 2, 1, 3).reshape(u * bs, hkv, d)
-    slots = (pool.used_blocks.astype(np.int64)[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)
-    bad = np.isnan(_floats(kr, pool.dtype)).any(axis=(1, 2)) | np.isnan(_floats(vr, pool.dtype)).any(axis=(1, 2))
-    return kr, vr, np.where(bad, -1, slots).astype(np.int32)
-
-
 def garbage_int8_pool(nb, hkv, bs, d, seed, device="cuda"):
     g = torch.Generator(device="cpu").manual_seed(seed)
     kc = torch.randint(-128, 128, (nb, hkv, bs, d), dtype=torch.int8, generator=g).to(device)
@@ -86,7 +75,7 @@ def test_store_int8_bit_exact(pkv, orc, dtype, d):
 def run_int8_decode(pkv, orc, c, seqs=None):
     """GPU: quantize every cached row and the new token into an int8 pool of garbage, then decode.
     Oracle: the same quantization into host arrays, dequantize, float64 decode."""
-    kr, vr, slots = cached_rows(c.pool)
+    kr, vr, slots = W.cached_rows(c.pool)
     kc, vc, ks, vs = garbage_int8_pool(c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim, c.seed)
     for k_, v_, s_ in ((kr, vr, slots), (c.key, c.value, c.slot_mapping)):
         pkv.kv_cache_store_int8(to_torch(k_, c.dtype), to_torch(v_, c.dtype), kc, vc, ks, vs, i32(s_))

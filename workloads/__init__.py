@@ -151,6 +151,19 @@ class Pool:
         return kc, vc
 
 
+def cached_rows(pool: "Pool"):
+    """Every row of the pool's owned blocks as store input: K and V ``[N, Hkv, D]`` (storage dtype) and
+    the slot of each row (block * block_size + offset); rows not holding a cached token (NaN) get slot
+    -1. Used to fill a cache of another element type through its own store call."""
+    u, hkv, bs, d = pool.key_blocks.shape
+    kr = pool.key_blocks.transpose(0, 2, 1, 3).reshape(u * bs, hkv, d)
+    vr = pool.value_blocks.transpose(0, 2, 1, 3).reshape(u * bs, hkv, d)
+    slots = (pool.used_blocks.astype(np.int64)[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)
+    as_f = (lambda a: bf16_bits_to_f32(a)) if pool.dtype == BF16 else (lambda a: np.asarray(a, np.float32))
+    bad = np.isnan(as_f(kr)).any(axis=(1, 2)) | np.isnan(as_f(vr)).any(axis=(1, 2))
+    return kr, vr, np.where(bad, -1, slots).astype(np.int32)
+
+
 @dataclass
 class DecodeCase:
     """One decode step: store one new token per sequence, then attend over ``context_lens``."""
