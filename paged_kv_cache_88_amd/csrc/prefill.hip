@@ -48,6 +48,7 @@ constexpr int PF_KPAD = PF_D + 8;         // LDS row stride of K, bf16 elements 
 constexpr int PF_VPAD = PF_BN + 4;        // LDS row stride of V^T (136 bytes: 16 rows fall on distinct bank pairs)
 constexpr float PF_M_INIT = -1.0e30f;
 constexpr int PF_XCDS = 8;                // MI355X: 8 XCDs, each with its own L2
+constexpr int PF_BUF_W3 = 0x00020000;     // buffer descriptor word 3: raw, untyped buffer (gfx9 family)
 
 template <int G>
 __global__ void __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -60,15 +61,17 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
     constexpr int VR = BQ * G;                // rows in use (<= 128)
     constexpr int CH = PF_D / 8;              // 16-byte chunks per K/V row
 
-    __shared__ __attribute__((aligned(16))) uint16_t sK[PF_BN * PF_KPAD];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[PF_D * PF_VPAD];
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][PF_BN * PF_KPAD];     // double-buffered tiles
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][PF_D * PF_VPAD];
 
     // linear id w runs on XCD w % 8: group g = (sequence, kv head) lives on XCD g % 8
     const int w = blockIdx.x, xcd = w & (PF_XCDS - 1), j = w / PF_XCDS;
-    const int g = (j / num_q_tiles) * PF_XCDS + xcd;
+    // (divisions run on the vector ALU; readfirstlane states that the results are wave-uniform, so
+    // addresses built from them stay in scalar registers)
+    const int g = __builtin_amdgcn_readfirstlane((j / num_q_tiles) * PF_XCDS + xcd);
     if (g >= num_seqs * num_kv_heads) return;
-    const int qt = num_q_tiles - 1 - j % num_q_tiles;
-    const int seq = g / num_kv_heads, kvh = g % num_kv_heads;
+    const int qt = __builtin_amdgcn_readfirstlane(num_q_tiles - 1 - j % num_q_tiles);
+    const int seq = __builtin_amdgcn_readfirstlane(g / num_kv_heads), kvh = __builtin_amdgcn_readfirstlane(g % num_kv_heads);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lb = lane >> 4;       // MFMA lane row / lane block
     const int num_heads = num_kv_heads * G;
@@ -105,19 +108,31 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
     // 16 lanes of a row group on consecutive key groups so their V^T stores fill 128 contiguous bytes
     const int vkg = tid & 15, vdg = tid >> 4;
     u32x4 kreg[4], vreg[4];
+    // the first 64 block ids of the sequence, one per lane (uniform tiles read them with readlane)
+    const int nblk_seq = (Lk + bs_mask) >> log2_bs;
+    const int my_blk = lane < nblk_seq ? bt[lane] : -1;
     auto load_tile = [&](int key0) {
         if (log2_bs >= 6 && key0 + PF_BN <= kend) {
-            // the whole tile lies in one block (64 | block_size, tiles start at multiples of 64)
-            const int64_t blk = bt[key0 >> log2_bs];
+            // The whole tile lies in one block (64 | block_size, tiles start at multiples of 64): one buffer
+            // descriptor for the (block, kv head) slab, the tile's row as scalar offset, lane offsets fixed.
+            // A block id outside the pool gets an empty descriptor, whose loads return zeros.
+            const int j = key0 >> log2_bs;
+            // (readfirstlane: the id is wave-uniform; saying so keeps the descriptor in scalar registers)
+            const int64_t blk = __builtin_amdgcn_readfirstlane(j < 64 ? __builtin_amdgcn_readlane(my_blk, j) : bt[j]);
             const bool ok = blk >= 0 && blk < num_blocks;
-            const int64_t base = ((((ok ? blk : 0) * num_kv_heads + kvh) << log2_bs) + (key0 & bs_mask)) * CH;
+            const int64_t slab = ((ok ? blk : 0) * num_kv_heads + kvh) << log2_bs;       // first row
+            const int range = ok ? (int)((uint32_t)PF_D * 2u << log2_bs) : 0;
+            const __amdgpu_buffer_rsrc_t kr =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(key_cache + slab * CH), (short)0, range, PF_BUF_W3);
+            const __amdgpu_buffer_rsrc_t vr =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(value_cache + slab * CH), (short)0, range, PF_BUF_W3);
+            const int soff = (key0 & bs_mask) * PF_D * 2;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int idx = tid + c * PF_THREADS;
-                kreg[c] = ok ? key_cache[base + idx] : u32x4{0, 0, 0, 0};
-            }
+            for (int c = 0; c < 4; ++c)
+                kreg[c] = __builtin_amdgcn_raw_buffer_load_b128(kr, (tid + c * PF_THREADS) * 16, soff, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) vreg[i] = ok ? value_cache[base + (vkg * 4 + i) * CH + vdg] : u32x4{0, 0, 0, 0};
+            for (int i = 0; i < 4; ++i)
+                vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, ((vkg * 4 + i) * CH + vdg) * 16, soff, 0);
             return;
         }
 #pragma unroll
@@ -142,19 +157,19 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
             }
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int buf) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int idx = tid + c * PF_THREADS;
-            *(u32x4 *)&sK[(idx / CH) * PF_KPAD + (idx % CH) * 8] = kreg[c];
+            *(u32x4 *)&sK[buf][(idx / CH) * PF_KPAD + (idx % CH) * 8] = kreg[c];
         }
         // V^T: dim 8*vdg + 2j (+1) gets keys 4*vkg..+4 as two bf16 pairs
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const u32x2 lo = u32x2{pair_lo(vreg[0][j], vreg[1][j]), pair_lo(vreg[2][j], vreg[3][j])};
             const u32x2 hi = u32x2{pair_hi(vreg[0][j], vreg[1][j]), pair_hi(vreg[2][j], vreg[3][j])};
-            *(u32x2 *)&sV[(vdg * 8 + 2 * j) * PF_VPAD + vkg * 4] = lo;
-            *(u32x2 *)&sV[(vdg * 8 + 2 * j + 1) * PF_VPAD + vkg * 4] = hi;
+            *(u32x2 *)&sV[buf][(vdg * 8 + 2 * j) * PF_VPAD + vkg * 4] = lo;
+            *(u32x2 *)&sV[buf][(vdg * 8 + 2 * j + 1) * PF_VPAD + vkg * 4] = hi;
         }
     };
 
@@ -169,10 +184,10 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
     }
 
     load_tile(0);
-    store_tile();
+    store_tile(0);
     __syncthreads();
     for (int kt = 0; kt < ntiles; ++kt) {
-        const int key0 = kt * PF_BN;
+        const int key0 = kt * PF_BN, cur = kt & 1;
         if (kt + 1 < ntiles) load_tile(key0 + PF_BN);      // in flight during this tile's math
 
         // S^T = K Q^T: s[kb][qb] holds keys 16*kb + 4*lb + i of row 16*qb + lr
@@ -183,7 +198,7 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
             s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const u32x4 ka = *(const u32x4 *)&sK[(kb * 16 + lr) * PF_KPAD + lb * 8 + ks * 32];
+                const u32x4 ka = *(const u32x4 *)&sK[cur][(kb * 16 + lr) * PF_KPAD + lb * 8 + ks * 32];
                 s[kb][0] = mfma16x16x32(ka, qb_reg[0][ks], s[kb][0]);
                 s[kb][1] = mfma16x16x32(ka, qb_reg[1][ks], s[kb][1]);
             }
@@ -192,7 +207,7 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
         // mask, online softmax per row, rounded weights packed as the B operand of O^T += V^T P^T
         // (scores stay unscaled until the exponent: scale > 0 keeps the max; m is kept in scaled units)
         const bool masked = key0 + PF_BN > kfull;            // some key of this tile is hidden from a row
-        if (masked) {
+        if (masked) [[unlikely]] {
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -254,7 +269,7 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
-                const uint16_t *vrow = &sV[(db * 16 + lr) * PF_VPAD + ks * 32 + lb * 4];
+                const uint16_t *vrow = &sV[cur][(db * 16 + lr) * PF_VPAD + ks * 32 + lb * 4];
                 const u32x2 a0 = *(const u32x2 *)vrow;
                 const u32x2 a1 = *(const u32x2 *)(vrow + 16);
                 const u32x4 va = u32x4{a0[0], a0[1], a1[0], a1[1]};
@@ -262,11 +277,9 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
                 o[db][1] = mfma16x16x32(va, pb[ks][1], o[db][1]);
             }
         }
-        __syncthreads();                                     // every wave is done with this tile
-        if (kt + 1 < ntiles) {
-            store_tile();
-            __syncthreads();
-        }
+        // the next tile goes to the other buffer, which every wave finished reading before the last barrier
+        if (kt + 1 < ntiles) store_tile(cur ^ 1);
+        __syncthreads();            // the next tile is in LDS, and every wave is done with this one
     }
 
     // normalise and write: lane holds dims 16*db + 4*lb + i of row 16*qb + lr
