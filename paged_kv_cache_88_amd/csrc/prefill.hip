@@ -33,6 +33,8 @@
 // The MFMA output layout is the 16x16 fp32 block with lane l holding rows 4*(l/16)+i, column l%16;
 // the A/B operands take 8 reduction elements per lane, paired between the operands element by
 // element, so any reduction order of the hardware sums matching pairs.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -42,23 +44,26 @@ namespace pkv {
 constexpr int PF_THREADS = 256;
 constexpr int PF_D = 128;
 constexpr int PF_BN = 64;                 // keys per tile
-constexpr int PF_ROWS = 128;              // rows per workgroup
-constexpr int PF_WROWS = 32;              // rows per wave
 constexpr int PF_KPAD = PF_D + 8;         // LDS row stride of K, bf16 elements (272 bytes)
 constexpr int PF_VPAD = PF_BN + 4;        // LDS row stride of V^T (136 bytes: 16 rows fall on distinct bank pairs)
 constexpr float PF_M_INIT = -1.0e30f;
+constexpr float PF_RESCALE_SLACK = 8.0f;  // weights stay <= 256 between rescales
 constexpr int PF_XCDS = 8;                // MI355X: 8 XCDs, each with its own L2
 constexpr int PF_BUF_W3 = 0x00020000;     // buffer descriptor word 3: raw, untyped buffer (gfx9 family)
 
-template <int G>
-__global__ void __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// QB: 16-row blocks per wave (rows per wave 16 QB, per workgroup 64 QB). Every K and V^T value read from
+// LDS feeds QB MFMAs, so LDS traffic per MFMA falls as QB grows; QB = 4 takes one wave per SIMD.
+template <int G, int QB>
+__global__ void __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(QB <= 2 ? 2 : 1, QB <= 2 ? 2 : 1)))
 prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, const u32x4 *__restrict__ key_cache,
                const u32x4 *__restrict__ value_cache, const int32_t *__restrict__ block_tables, int bt_stride,
                const int32_t *__restrict__ cu_seqlens_q, const int32_t *__restrict__ cu_seqlens_k, int num_seqs,
                int max_seqlen_k, int num_q_tiles, int num_kv_heads, int64_t num_blocks, int log2_bs, float scale_log2e,
                int causal) {
-    constexpr int BQ = PF_ROWS / G;           // query positions per workgroup
-    constexpr int VR = BQ * G;                // rows in use (<= 128)
+    constexpr int WROWS = 16 * QB;            // rows per wave
+    constexpr int ROWS = 4 * WROWS;           // rows per workgroup
+    constexpr int BQ = ROWS / G;              // query positions per workgroup
+    constexpr int VR = BQ * G;                // rows in use (<= ROWS)
     constexpr int CH = PF_D / 8;              // 16-byte chunks per K/V row
 
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][PF_BN * PF_KPAD];     // double-buffered tiles
@@ -89,13 +94,13 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
     const int bs_mask = (1 << log2_bs) - 1;
     const int32_t *bt = block_tables + (int64_t)seq * bt_stride;
 
-    // this lane's two query rows (one per 16-row block qb): row = wave*32 + 16*qb + lr
-    int kmax[2];
-    bool row_ok[2];
-    u32x4 qb_reg[2][4];                       // B operand of S^T: dims 8*lb + 32*ks .. +8 of the row
+    // this lane's QB query rows (one per 16-row block qb): row = wave * WROWS + 16*qb + lr
+    int kmax[QB];
+    bool row_ok[QB];
+    u32x4 qb_reg[QB][4];                      // B operand of S^T: dims 8*lb + 32*ks .. +8 of the row
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int r = wave * PF_WROWS + qb * 16 + lr;
+    for (int qb = 0; qb < QB; ++qb) {
+        const int r = wave * WROWS + qb * 16 + lr;
         const int pos = r / G, h = r % G;
         row_ok[qb] = r < VR && pos < npos;
         kmax[qb] = causal ? P + pos0 + pos : Lk - 1;
@@ -173,10 +178,10 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
         }
     };
 
-    f32x4 o[8][2];                            // O^T blocks: dims 16*db + 4*lb + i, row 16*qb + lr
-    float m[2], l[2];
+    f32x4 o[8][QB];                           // O^T blocks: dims 16*db + 4*lb + i, row 16*qb + lr
+    float m[QB], l[QB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
         m[qb] = PF_M_INIT;
@@ -186,30 +191,33 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
     load_tile(0);
     store_tile(0);
     __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
+    // One tile: load the next, Sᵀ, (mask), softmax, Oᵀ += VᵀPᵀ, store the next. MASKED is a compile-time
+    // flag: tiles wholly below every row's causal bound and the sequence end (the first nfull) run a body
+    // with no mask code at all.
+    auto tile_step = [&](int kt, auto masked_flag) {
+        constexpr bool MASKED = decltype(masked_flag)::value;
         const int key0 = kt * PF_BN, cur = kt & 1;
         if (kt + 1 < ntiles) load_tile(key0 + PF_BN);      // in flight during this tile's math
 
         // S^T = K Q^T: s[kb][qb] holds keys 16*kb + 4*lb + i of row 16*qb + lr
-        f32x4 s[4][2];
+        f32x4 s[4][QB];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            s[kb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-            s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const u32x4 ka = *(const u32x4 *)&sK[cur][(kb * 16 + lr) * PF_KPAD + lb * 8 + ks * 32];
-                s[kb][0] = mfma16x16x32(ka, qb_reg[0][ks], s[kb][0]);
-                s[kb][1] = mfma16x16x32(ka, qb_reg[1][ks], s[kb][1]);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma16x16x32(ka, qb_reg[qb][ks], s[kb][qb]);
             }
         }
 
         // mask, online softmax per row, rounded weights packed as the B operand of O^T += V^T P^T
         // (scores stay unscaled until the exponent: scale > 0 keeps the max; m is kept in scaled units)
-        const bool masked = key0 + PF_BN > kfull;            // some key of this tile is hidden from a row
-        if (masked) [[unlikely]] {
+        if constexpr (MASKED) {                              // some key of this tile is hidden from a row
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
+            for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -218,10 +226,10 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
                         if (!(row_ok[qb] && key <= kmax[qb])) s[kb][qb][i] = -INFINITY;
                     }
         }
-        float m_new[2];
+        float m_new[QB];
         bool grow = false;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
@@ -229,11 +237,15 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             m_new[qb] = fmaxf(m[qb], mx * scale_log2e);
-            grow |= m_new[qb] > m[qb];
+            grow |= m_new[qb] > m[qb] + PF_RESCALE_SLACK;
         }
-        if (__builtin_amdgcn_ballot_w64(grow)) {             // rescale only when a running max grew
+        // Rescale only when some row's max passes its reference m by more than PF_RESCALE_SLACK (log2 units);
+        // otherwise m stays as is, and weights 2^(s - m) reach at most 2^PF_RESCALE_SLACK. The final
+        // division by l, summed with the same reference, makes the result independent of m.
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            asm volatile("" ::: "memory");                   // a real branch, not speculated multiplies
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
+            for (int qb = 0; qb < QB; ++qb) {
                 const float alpha = fast_exp2(m[qb] - m_new[qb]);
                 l[qb] *= alpha;
 #pragma unroll
@@ -241,9 +253,9 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
                 m[qb] = m_new[qb];
             }
         }
-        u32x4 pb[2][2];                                      // [ks][qb]
+        u32x4 pb[2][QB];                                     // [ks][qb]
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
             const float nm = -m[qb];
             float rs = 0.f;
 #pragma unroll
@@ -273,22 +285,25 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
                 const u32x2 a0 = *(const u32x2 *)vrow;
                 const u32x2 a1 = *(const u32x2 *)(vrow + 16);
                 const u32x4 va = u32x4{a0[0], a0[1], a1[0], a1[1]};
-                o[db][0] = mfma16x16x32(va, pb[ks][0], o[db][0]);
-                o[db][1] = mfma16x16x32(va, pb[ks][1], o[db][1]);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma16x16x32(va, pb[ks][qb], o[db][qb]);
             }
         }
         // the next tile goes to the other buffer, which every wave finished reading before the last barrier
         if (kt + 1 < ntiles) store_tile(cur ^ 1);
         __syncthreads();            // the next tile is in LDS, and every wave is done with this one
-    }
+    };
+    const int nfull = min(ntiles, kfull / PF_BN);             // tiles with every key visible to every row
+    for (int kt = 0; kt < nfull; ++kt) tile_step(kt, std::integral_constant<bool, false>{});
+    for (int kt = nfull; kt < ntiles; ++kt) tile_step(kt, std::integral_constant<bool, true>{});
 
     // normalise and write: lane holds dims 16*db + 4*lb + i of row 16*qb + lr
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         float lsum = l[qb];
         lsum += __shfl_xor(lsum, 16);
         lsum += __shfl_xor(lsum, 32);
-        const int r = wave * PF_WROWS + qb * 16 + lr;
+        const int r = wave * WROWS + qb * 16 + lr;
         const int pos = r / G, h = r % G;
         if (!row_ok[qb]) continue;
         const float inv = 1.0f / lsum;
@@ -302,13 +317,18 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
     }
 }
 
+#ifndef PKV_PREFILL_QB
+#define PKV_PREFILL_QB 2
+#endif
+
 template <int G>
 static hipError_t launch_prefill_g(const PrefillArgs &a, hipStream_t stream) {
-    constexpr int BQ = PF_ROWS / G;
+    constexpr int QB = PKV_PREFILL_QB;
+    constexpr int BQ = 64 * QB / G;
     const int num_q_tiles = (a.max_seqlen_q + BQ - 1) / BQ;
     const int64_t groups = (int64_t)a.num_seqs * a.num_kv_heads;
     const int64_t wgs = (groups + PF_XCDS - 1) / PF_XCDS * PF_XCDS * num_q_tiles;
-    hipLaunchKernelGGL((prefill_kernel<G>), dim3((unsigned)wgs), dim3(PF_THREADS), 0, stream, (uint16_t *)a.out,
+    hipLaunchKernelGGL((prefill_kernel<G, QB>), dim3((unsigned)wgs), dim3(PF_THREADS), 0, stream, (uint16_t *)a.out,
                        (const u32x4 *)a.query, (const u32x4 *)a.key_cache, (const u32x4 *)a.value_cache, a.block_tables,
                        a.bt_stride, a.cu_seqlens_q, a.cu_seqlens_k, a.num_seqs, a.max_seqlen_k, num_q_tiles,
                        a.num_kv_heads, a.num_blocks, a.log2_bs, a.scale_log2e, a.causal);
