@@ -202,8 +202,8 @@ size_t pkv_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_h
 
 namespace {
 
-// Validation and argument set-up shared by the decode entry points (cache element bytes: 4, 2 or 1).
-pkv_status decode_args(pkv::DecodeArgs &a, pkv_dtype dtype, int cache_elem_bytes, void *out, const void *query,
+// Validation and argument set-up shared by the decode entry points.
+pkv_status decode_args(pkv::DecodeArgs &a, pkv_dtype dtype, void *out, const void *query,
                        const void *key_cache, const void *value_cache, const int32_t *block_tables,
                        int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
                        int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -225,7 +225,6 @@ pkv_status decode_args(pkv::DecodeArgs &a, pkv_dtype dtype, int cache_elem_bytes
     REQUIRE(block_tables || max_context_len == 0, PKV_EINVAL, "null block_tables");
     REQUIRE(aligned16(out) && aligned16(query) && aligned16(key_cache) && aligned16(value_cache), PKV_EINVAL,
             "out, query and cache pointers must be 16-byte aligned");
-    (void)cache_elem_bytes;
     DecodePlan plan = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len);
     REQUIRE((int64_t)num_seqs * (((int64_t)max_context_len + 31) / 32) < ((int64_t)1 << 30), PKV_EINVAL,
             "num_seqs * max_context_len too large (at most 2^35 tokens)");
@@ -273,7 +272,7 @@ pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *qu
                                       int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
                                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
     pkv::DecodeArgs a;
-    pkv_status st = decode_args(a, dtype, elem_bytes(dtype), out, query, key_cache, value_cache, block_tables,
+    pkv_status st = decode_args(a, dtype, out, query, key_cache, value_cache, block_tables,
                                 block_table_stride, context_lens, num_seqs, max_context_len, num_heads, num_kv_heads,
                                 head_dim, block_size, num_blocks, scale, workspace, workspace_bytes);
     if (st != PKV_OK || num_seqs == 0) return st;
@@ -312,7 +311,7 @@ pkv_status pkv_paged_attention_decode_int8(pkv_dtype dtype, void *out, const voi
     REQUIRE(head_dim == 128, PKV_EUNSUPPORTED, "int8-cache decode supports head_dim 128 (got %d)", head_dim);
     REQUIRE(block_size >= 16, PKV_EUNSUPPORTED, "int8-cache decode needs block_size >= 16 (got %d)", block_size);
     pkv::DecodeArgs a;
-    pkv_status st = decode_args(a, dtype, 1, out, query, key_cache, value_cache, block_tables, block_table_stride,
+    pkv_status st = decode_args(a, dtype, out, query, key_cache, value_cache, block_tables, block_table_stride,
                                 context_lens, num_seqs, max_context_len, num_heads, num_kv_heads, head_dim, block_size,
                                 num_blocks, scale, workspace, workspace_bytes);
     if (st != PKV_OK || num_seqs == 0) return st;

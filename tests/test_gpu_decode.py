@@ -95,6 +95,32 @@ def test_mixed_long_and_short(pkv, orc):
     assert_close(got[seqs], oracle_decode_case(orc, c, seqs=seqs), W.BF16, "mixed")
 
 
+def test_maximum_batch(pkv, orc):
+    """65535 sequences (the ABI's limit) of 1 to 40 tokens with a few empty ones, fp32, head_dim 64:
+    the plan's scan runs over 64 chunks, most of them past the register-resident part."""
+    rng = np.random.default_rng(65535)
+    b = 65535
+    lens = rng.integers(1, 41, size=b).astype(np.int32)
+    lens[rng.choice(b, 7, replace=False)] = 0
+    nb = int(sum(W.blocks_for_tokens(int(n), 16) for n in lens)) + 1
+    c = W.make_decode_case("maxbatch", 99, W.F32, lens, 4, 2, 64, 16, nb, rng=rng)
+    got, _, _ = run_decode_case(pkv, c)
+    seqs = np.array(sorted(set(rng.choice(b, 30, replace=False).tolist()) | {0, b - 1} |
+                           set(np.flatnonzero(lens == 0).tolist())), np.int32)
+    assert np.abs(got[seqs] - oracle_decode_case(orc, c, seqs=seqs)).max() <= 1e-5
+    assert np.all(got[lens == 0] == 0)
+
+
+def test_last_blocks_of_the_pool(pkv, orc):
+    """Block tables that use the last physical blocks of a pool exactly its size (no spare block)."""
+    lens = [256, 255, 1]
+    nb = sum(W.blocks_for_tokens(n, 256) for n in lens)
+    c = W.make_decode_case("lastblocks", 5, W.BF16, lens, 16, 2, 128, 256, nb)
+    assert c.block_tables.max() == nb - 1
+    got, _, _ = run_decode_case(pkv, c)
+    assert_close(got, oracle_decode_case(orc, c), W.BF16, "last blocks")
+
+
 def test_empty_context_gives_zeros(pkv, orc):
     c = W.make_decode_case("empty", 7, W.BF16, [0, 5, 0, 600], 8, 2, 128, 16, 64)
     got, _, _ = run_decode_case(pkv, c)
