@@ -880,8 +880,9 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
 // out = sum_p w_p o_p / sum_p w_p l_p. A workgroup serves `hpb` heads of one sequence (hpb in {1, 2, 4, 8},
 // chosen so the grid has a few thousand workgroups: with many sequences most have one part and their
 // workgroups exit after one load). Its threads are hpb heads x PL = 8 / hpb part lanes x D/4 dim groups:
-// a thread sums dims 4 dg .. +4 over the parts p = pl mod PL with 16-byte loads, and the part lanes are
-// added through LDS. Sequences of one part were written by the decode kernel.
+// a thread merges dims 4 dg .. +4 of the parts p = pl mod PL with 16-byte loads (running max, so each
+// part's m, l, o load in one round trip), and the part lanes are merged through LDS by the same rule.
+// Sequences of one part were written by the decode kernel.
 constexpr int REDUCE_THREADS = 256;
 
 template <bool BF16, int D>
@@ -890,7 +891,7 @@ decode_reduce_kernel(void *__restrict__ out, const int4 *__restrict__ seq_info, 
                      const float *__restrict__ ws_m, const float *__restrict__ ws_l, const float *__restrict__ ws_o) {
     constexpr int DG = D / 4, SLOTS = REDUCE_THREADS / DG;          // SLOTS = head slots x part lanes
     __shared__ f32x4 s_o[SLOTS][DG];
-    __shared__ float s_l[SLOTS];
+    __shared__ float s_l[SLOTS], s_m[SLOTS];
     const int seq = blockIdx.y;
     const int4 si = seq_info[seq];
     const int nparts = si.y;
@@ -902,26 +903,36 @@ decode_reduce_kernel(void *__restrict__ out, const int4 *__restrict__ seq_info, 
     const bool active = head < num_heads;
     float ll = 0.f;
     f32x4 oo = {0.f, 0.f, 0.f, 0.f};
+    // one pass per part lane with a running max (each part's m, l and o load together), then the part
+    // lanes are merged with the same rule through LDS
+    float mm = M_INIT;
     if (active) {
         const int64_t p0 = (int64_t)si.x * num_heads + head;     // part p sits at p0 + p * num_heads
-        float mm = M_INIT;
-#pragma unroll 8
-        for (int p = 0; p < nparts; ++p) mm = fmaxf(mm, ws_m[p0 + (int64_t)p * num_heads]);
 #pragma unroll 2
         for (int p = pl; p < nparts; p += PL) {
             const int64_t pi = p0 + (int64_t)p * num_heads;
-            const float w = fast_exp2(ws_m[pi] - mm);
-            ll += ws_l[pi] * w;
-            oo += w * *(const f32x4 *)(ws_o + pi * D + 4 * dg);
+            const float mp = ws_m[pi], lp = ws_l[pi];
+            const f32x4 op = *(const f32x4 *)(ws_o + pi * D + 4 * dg);
+            const float mn = fmaxf(mm, mp);
+            const float a = fast_exp2(mm - mn), w = fast_exp2(mp - mn);
+            ll = ll * a + lp * w;
+            oo = oo * a + op * w;
+            mm = mn;
         }
     }
     s_o[slot][dg] = oo;
-    if (dg == 0) s_l[slot] = ll;
+    if (dg == 0) {
+        s_l[slot] = ll;
+        s_m[slot] = mm;
+    }
     __syncthreads();
     if (pl != 0 || !active) return;
     for (int q = 1; q < PL; ++q) {
-        oo += s_o[slot + q][dg];
-        ll += s_l[slot + q];
+        const float mq = s_m[slot + q], mn = fmaxf(mm, mq);
+        const float a = fast_exp2(mm - mn), w = fast_exp2(mq - mn);
+        oo = oo * a + s_o[slot + q][dg] * w;
+        ll = ll * a + s_l[slot + q] * w;
+        mm = mn;
     }
     const float inv = 1.0f / ll;
     const int64_t o = ((int64_t)seq * num_heads + head) * D + 4 * dg;
