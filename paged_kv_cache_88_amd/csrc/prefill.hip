@@ -20,16 +20,16 @@
 // so each K/V tile brought into LDS serves all G heads. Each wave owns 32 rows. The key loop walks
 // 64-key tiles up to the last key any row of the tile may see; the next tile's K/V rows are loaded
 // into registers while the current tile is computed.
-//   - Gather: K rows go to LDS row-major; each thread transposes a 4-key x 8-dim piece of V in
-//     registers (v_perm) and stores it key-contiguous, so LDS holds V^T.
+//   - Gather: K and V rows both go to LDS row-major (16-byte stores, no transposition in registers).
 //   - S^T = K Q^T on MFMA: K (LDS) is the A operand, Q (registers) the B operand. In the 16x16
 //     output block lane l holds keys 4*(l/16)+i of query row l%16.
 //   - Mask (causal, bottom-right aligned; sequence end), online softmax per query row in log2 units:
 //     a row's 64 scores sit in 16 values of each of 4 lanes (lane, lane^16, lane^32, lane^48).
 //   - O^T += V^T P^T on MFMA: the rounded weights of S^T's registers are already laid out as the B
 //     operand (a lane's 8 reduction elements are keys {4b..4b+3} and {16+4b..16+4b+3} of a 32-key
-//     step, b = l/16), and V^T is read from LDS with the same key order as the A operand. P never
-//     goes through LDS.
+//     step, b = l/16), and V^T comes out of the row-major V tile through ds_read_b64_tr_b16, the
+//     gfx950 transposing LDS read (in a 16-lane group, lane i receives element i % 4 of the 8-byte
+//     chunks read by lanes 4k + i / 4, k = 0..3), in the same key order. P never goes through LDS.
 // The MFMA output layout is the 16x16 fp32 block with lane l holding rows 4*(l/16)+i, column l%16;
 // the A/B operands take 8 reduction elements per lane, paired between the operands element by
 // element, so any reduction order of the hardware sums matching pairs.
@@ -45,11 +45,18 @@ constexpr int PF_THREADS = 256;
 constexpr int PF_D = 128;
 constexpr int PF_BN = 64;                 // keys per tile
 constexpr int PF_KPAD = PF_D + 8;         // LDS row stride of K, bf16 elements (272 bytes)
-constexpr int PF_VPAD = PF_BN + 4;        // LDS row stride of V^T (136 bytes: 16 rows fall on distinct bank pairs)
 constexpr float PF_M_INIT = -1.0e30f;
 constexpr float PF_RESCALE_SLACK = 8.0f;  // weights stay <= 256 between rescales
 constexpr int PF_XCDS = 8;                // MI355X: 8 XCDs, each with its own L2
 constexpr int PF_BUF_W3 = 0x00020000;     // buffer descriptor word 3: raw, untyped buffer (gfx9 family)
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 at an LDS address (8 bytes, 8-byte aligned), as two dwords.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *p) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)p);
+    return __builtin_bit_cast(u32x2, v);
+}
 
 // QB: 16-row blocks per wave (rows per wave 16 QB, per workgroup 64 QB). Every K and V^T value read from
 // LDS feeds QB MFMAs, so LDS traffic per MFMA falls as QB grows; QB = 4 takes one wave per SIMD.
@@ -67,7 +74,7 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
     constexpr int CH = PF_D / 8;              // 16-byte chunks per K/V row
 
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][PF_BN * PF_KPAD];     // double-buffered tiles
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][PF_D * PF_VPAD];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][PF_BN * PF_KPAD];
 
     // linear id w runs on XCD w % 8: group g = (sequence, kv head) lives on XCD g % 8
     const int w = blockIdx.x, xcd = w & (PF_XCDS - 1), j = w / PF_XCDS;
@@ -109,9 +116,7 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
         for (int ks = 0; ks < 4; ++ks) qb_reg[qb][ks] = row_ok[qb] ? query[qrow + lb + 4 * ks] : u32x4{0, 0, 0, 0};
     }
 
-    // gather roles: K chunks tid + 256*c (c < 4); V piece = keys 4*vkg..+4 x dims 8*vdg..+8, with the
-    // 16 lanes of a row group on consecutive key groups so their V^T stores fill 128 contiguous bytes
-    const int vkg = tid & 15, vdg = tid >> 4;
+    // gather roles: thread tid moves 16-byte chunks tid + 256 c (c < 4) of the K and of the V tile
     u32x4 kreg[4], vreg[4];
     // the first 64 block ids of the sequence, one per lane (uniform tiles read them with readlane)
     const int nblk_seq = (Lk + bs_mask) >> log2_bs;
@@ -136,29 +141,22 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
             for (int c = 0; c < 4; ++c)
                 kreg[c] = __builtin_amdgcn_raw_buffer_load_b128(kr, (tid + c * PF_THREADS) * 16, soff, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, ((vkg * 4 + i) * CH + vdg) * 16, soff, 0);
+            for (int c = 0; c < 4; ++c)
+                vreg[c] = __builtin_amdgcn_raw_buffer_load_b128(vr, (tid + c * PF_THREADS) * 16, soff, 0);
             return;
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int idx = tid + c * PF_THREADS;
             const int gk = key0 + idx / CH, ch = idx % CH;
-            kreg[c] = u32x4{0, 0, 0, 0};
+            kreg[c] = vreg[c] = u32x4{0, 0, 0, 0};
             if (gk < kend) {
                 const int64_t blk = bt[gk >> log2_bs];
-                if (blk >= 0 && blk < num_blocks)
-                    kreg[c] = key_cache[(((blk * num_kv_heads + kvh) << log2_bs) + (gk & bs_mask)) * CH + ch];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int gk = key0 + vkg * 4 + i;
-            vreg[i] = u32x4{0, 0, 0, 0};
-            if (gk < kend) {
-                const int64_t blk = bt[gk >> log2_bs];
-                if (blk >= 0 && blk < num_blocks)
-                    vreg[i] = value_cache[(((blk * num_kv_heads + kvh) << log2_bs) + (gk & bs_mask)) * CH + vdg];
+                if (blk >= 0 && blk < num_blocks) {
+                    const int64_t row = ((blk * num_kv_heads + kvh) << log2_bs) + (gk & bs_mask);
+                    kreg[c] = key_cache[row * CH + ch];
+                    vreg[c] = value_cache[row * CH + ch];
+                }
             }
         }
     };
@@ -167,14 +165,7 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
         for (int c = 0; c < 4; ++c) {
             const int idx = tid + c * PF_THREADS;
             *(u32x4 *)&sK[buf][(idx / CH) * PF_KPAD + (idx % CH) * 8] = kreg[c];
-        }
-        // V^T: dim 8*vdg + 2j (+1) gets keys 4*vkg..+4 as two bf16 pairs
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const u32x2 lo = u32x2{pair_lo(vreg[0][j], vreg[1][j]), pair_lo(vreg[2][j], vreg[3][j])};
-            const u32x2 hi = u32x2{pair_hi(vreg[0][j], vreg[1][j]), pair_hi(vreg[2][j], vreg[3][j])};
-            *(u32x2 *)&sV[buf][(vdg * 8 + 2 * j) * PF_VPAD + vkg * 4] = lo;
-            *(u32x2 *)&sV[buf][(vdg * 8 + 2 * j + 1) * PF_VPAD + vkg * 4] = hi;
+            *(u32x4 *)&sV[buf][(idx / CH) * PF_KPAD + (idx % CH) * 8] = vreg[c];
         }
     };
 
@@ -276,14 +267,16 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
             l[qb] += rs;
         }
 
-        // O^T += V^T P^T: A operand = V^T rows (dims) with keys {4b..4b+3} and {16+4b..16+4b+3} of the step
+        // O^T += V^T P^T: A operand = V^T rows (dims) with keys {4b..4b+3} and {16+4b..16+4b+3} of the step.
+        // Lane (lr, b) points its transposing read at key 32 ks + 4 b + lr / 4 (+16 for the second half),
+        // dims 16 db + 4 (lr % 4) .. +4; it receives dim 16 db + lr of keys 4b .. 4b + 3 (+16).
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
-                const uint16_t *vrow = &sV[cur][(db * 16 + lr) * PF_VPAD + ks * 32 + lb * 4];
-                const u32x2 a0 = *(const u32x2 *)vrow;
-                const u32x2 a1 = *(const u32x2 *)(vrow + 16);
+                const uint16_t *vp = &sV[cur][(ks * 32 + lb * 4 + (lr >> 2)) * PF_KPAD + db * 16 + 4 * (lr & 3)];
+                const u32x2 a0 = lds_read_tr16(vp);
+                const u32x2 a1 = lds_read_tr16(vp + 16 * PF_KPAD);
                 const u32x4 va = u32x4{a0[0], a0[1], a1[0], a1[1]};
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma16x16x32(va, pb[ks][qb], o[db][qb]);
