@@ -44,13 +44,24 @@ namespace pkv {
 constexpr int PF_THREADS = 256;
 constexpr int PF_D = 128;
 constexpr int PF_BN = 64;                 // keys per tile
-constexpr int PF_KPAD = PF_D + 8;         // LDS row stride of K, bf16 elements (272 bytes)
+constexpr int PF_KPAD = PF_D + 16;        // LDS row stride of the K and V tiles, bf16 elements (288 bytes)
 constexpr float PF_M_INIT = -1.0e30f;
 constexpr float PF_RESCALE_SLACK = 8.0f;  // weights stay <= 256 between rescales
+constexpr int PF_RANK_MAX = 64;           // batches ranked by length for the dispatch order
 constexpr int PF_XCDS = 8;                // MI355X: 8 XCDs, each with its own L2
 constexpr int PF_BUF_W3 = 0x00020000;     // buffer descriptor word 3: raw, untyped buffer (gfx9 family)
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Max over lanes l, l^16, l^32 and l^48 (one column of an MFMA result block), on the VALU: with both
+// operands the same register, v_permlane16_swap leaves lane l holding the values of lanes l & ~16 and
+// l | 16, and v_permlane32_swap those of lanes l & ~32 and l | 32.
+__device__ __forceinline__ float max_lane_blocks(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 // ds_read_b64_tr_b16 at an LDS address (8 bytes, 8-byte aligned), as two dwords.
 __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *p) {
@@ -76,15 +87,41 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][PF_BN * PF_KPAD];     // double-buffered tiles
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][PF_BN * PF_KPAD];
 
-    // linear id w runs on XCD w % 8: group g = (sequence, kv head) lives on XCD g % 8
+    // linear id w runs on XCD w % 8: group g = (sequence rank, kv head) lives on XCD g % 8
     const int w = blockIdx.x, xcd = w & (PF_XCDS - 1), j = w / PF_XCDS;
     // (divisions run on the vector ALU; readfirstlane states that the results are wave-uniform, so
     // addresses built from them stay in scalar registers)
     const int g = __builtin_amdgcn_readfirstlane((j / num_q_tiles) * PF_XCDS + xcd);
     if (g >= num_seqs * num_kv_heads) return;
     const int qt = __builtin_amdgcn_readfirstlane(num_q_tiles - 1 - j % num_q_tiles);
-    const int seq = __builtin_amdgcn_readfirstlane(g / num_kv_heads), kvh = __builtin_amdgcn_readfirstlane(g % num_kv_heads);
+    const int rank = __builtin_amdgcn_readfirstlane(g / num_kv_heads), kvh = __builtin_amdgcn_readfirstlane(g % num_kv_heads);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Dispatch order: workgroups start in linear-id order, and the sequence of rank r is the r-th longest
+    // (most keys; ties by index), so the longest work starts first and short work fills the tail. Each
+    // workgroup ranks the batch itself, one thread per sequence (batches of up to PF_RANK_MAX sequences;
+    // larger ones keep their order).
+    int seq = rank;
+    if (num_seqs > 1 && num_seqs <= PF_RANK_MAX) {
+        __shared__ int s_len[PF_RANK_MAX];
+        __shared__ int s_seq;
+        int lk = 0;
+        if (tid < num_seqs) {
+            lk = cu_seqlens_k[tid + 1] - cu_seqlens_k[tid];
+            s_len[tid] = lk;
+        }
+        __syncthreads();
+        if (tid < num_seqs) {
+            int r = 0;
+            for (int u = 0; u < num_seqs; ++u) {
+                const int lu = s_len[u];
+                r += (lu > lk) | ((lu == lk) & (u < tid));
+            }
+            if (r == rank) s_seq = tid;                     // ranks are a permutation: one thread writes
+        }
+        __syncthreads();
+        seq = s_seq;
+    }
+    seq = __builtin_amdgcn_readfirstlane(seq);
     const int lr = lane & 15, lb = lane >> 4;       // MFMA lane row / lane block
     const int num_heads = num_kv_heads * G;
 
@@ -225,8 +262,7 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
                 mx = fmaxf(fmaxf(mx, fmaxf(s[kb][qb][0], s[kb][qb][1])), fmaxf(s[kb][qb][2], s[kb][qb][3]));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = max_lane_blocks(mx);
             m_new[qb] = fmaxf(m[qb], mx * scale_log2e);
             grow |= m_new[qb] > m[qb] + PF_RESCALE_SLACK;
         }
