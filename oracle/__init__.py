@@ -69,8 +69,16 @@ class Oracle:
         lib.orc_quantize_int8.argtypes = [ctypes.c_int, P, I64, I32, P, P]
         lib.orc_store_int8.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, I64, I32, I32, I32, I64]
         lib.orc_dequantize_int8.argtypes = [P, P, I64, I32, P]
+        lib.orc_e4m3_value.argtypes = [ctypes.c_int]
+        lib.orc_e4m3_value.restype = ctypes.c_double
+        lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.orc_e4m3_encode.restype = ctypes.c_int
+        lib.orc_quantize_fp8.argtypes = [ctypes.c_int, P, I64, I32, P, P]
+        lib.orc_store_fp8.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, I64, I32, I32, I32, I64]
+        lib.orc_dequantize_fp8.argtypes = [P, P, I64, I32, P]
         for f in (lib.orc_store, lib.orc_gather, lib.orc_decode, lib.orc_prefill, lib.orc_quantize_int8,
-                  lib.orc_store_int8, lib.orc_dequantize_int8):
+                  lib.orc_store_int8, lib.orc_dequantize_int8, lib.orc_quantize_fp8, lib.orc_store_fp8,
+                  lib.orc_dequantize_fp8):
             f.restype = ctypes.c_int
         lib.orc_last_error.restype = ctypes.c_char_p
         lib.orc_max_threads.restype = ctypes.c_int
@@ -134,6 +142,51 @@ class Oracle:
             raise ValueError("one scale per row")
         out = np.empty(c.shape, dtype=np.float64)
         self._check(self.lib.orc_dequantize_int8(_ptr(c), _ptr(sc), c.size // d, d, _ptr(out)))
+        return out
+
+    def e4m3_value(self, code: int) -> float:
+        """Value of an OCP float8 E4M3 code (NaN for 0x7f and 0xff)."""
+        return self.lib.orc_e4m3_value(int(code))
+
+    def e4m3_encode(self, v: float) -> int:
+        """E4M3 code of the finite value nearest to float32 ``v`` (ties to an even mantissa)."""
+        return self.lib.orc_e4m3_encode(float(np.float32(v)))
+
+    def quantize_fp8(self, dtype, rows):
+        """E4M3 codes (uint8) and float32 scales of rows ``[..., D]`` (one scale per row): scale = max|x| / 448,
+        code = e4m3(x / scale) rounded half to even, in float32; zero rows give scale 0."""
+        sd = _store_dtype(dtype)
+        r = _c(rows, sd)
+        d = r.shape[-1]
+        n = r.size // d
+        codes = np.zeros(r.shape, dtype=np.uint8)
+        scales = np.zeros(r.shape[:-1], dtype=np.float32)
+        self._check(self.lib.orc_quantize_fp8(_DT[dtype], _ptr(r), n, d, _ptr(codes), _ptr(scales)))
+        return codes, scales
+
+    def store_fp8(self, dtype, key, value, key_cache, value_cache, key_scale, value_scale, slot_mapping):
+        """Quantize rows of key/value ``[N, Hkv, D]`` to E4M3 and scatter codes into the fp8 caches
+        ``[NB, Hkv, bs, D]`` (uint8) and scales into ``[NB, Hkv, bs]`` float32, in place (slots as in ``store``)."""
+        sd = _store_dtype(dtype)
+        for a, t in ((key_cache, np.uint8), (value_cache, np.uint8), (key_scale, np.float32), (value_scale, np.float32)):
+            if a.dtype != t or not a.flags.c_contiguous:
+                raise TypeError("fp8 caches (uint8) and float32 scales must be C-contiguous")
+        key, value = _c(key, sd), _c(value, sd)
+        sm = _c(slot_mapping, np.int32)
+        nb, hkv, bs, d = key_cache.shape
+        if key_scale.shape != (nb, hkv, bs) or value_scale.shape != (nb, hkv, bs):
+            raise ValueError("scale arrays must be [num_blocks, num_kv_heads, block_size]")
+        self._check(self.lib.orc_store_fp8(_DT[dtype], _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                           _ptr(key_scale), _ptr(value_scale), _ptr(sm), len(sm), hkv, d, bs, nb))
+
+    def dequantize_fp8(self, codes, scales):
+        """float64 values e4m3(code) * scale (exact) of fp8 rows ``[..., D]`` with scales ``[...]``."""
+        c, sc = _c(codes, np.uint8), _c(scales, np.float32)
+        d = c.shape[-1]
+        if sc.shape != c.shape[:-1]:
+            raise ValueError("one scale per row")
+        out = np.empty(c.shape, dtype=np.float64)
+        self._check(self.lib.orc_dequantize_fp8(_ptr(c), _ptr(sc), c.size // d, d, _ptr(out)))
         return out
 
     def copy_blocks(self, dtype, key_cache, value_cache, pairs):
@@ -247,3 +300,23 @@ def store_int8(*a, **k):
 
 def dequantize_int8(*a, **k):
     return default().dequantize_int8(*a, **k)
+
+
+def e4m3_value(*a, **k):
+    return default().e4m3_value(*a, **k)
+
+
+def e4m3_encode(*a, **k):
+    return default().e4m3_encode(*a, **k)
+
+
+def quantize_fp8(*a, **k):
+    return default().quantize_fp8(*a, **k)
+
+
+def store_fp8(*a, **k):
+    return default().store_fp8(*a, **k)
+
+
+def dequantize_fp8(*a, **k):
+    return default().dequantize_fp8(*a, **k)

@@ -11,6 +11,7 @@
  *   element dtype 0 = float32, 1 = bfloat16 (16-bit patterns, upcast exactly), 3 = float64
  *   int8 cache (orc_store_int8): codes [num_blocks][num_kv_heads][block_size][head_dim] int8 and one
  *   float32 scale per row, [num_blocks][num_kv_heads][block_size]
+ *   fp8 cache (orc_store_fp8): the same with one-byte E4M3 codes in place of int8
  *
  * Sources (web pages on the paged KV cache):
  *   - logical block j of a request lives in physical block block_table[j]; the kernel reads K/V
@@ -23,9 +24,10 @@
  *     ("LLM Infra 101 v0.2: KV Cache", section 推理);
  *   - chunked prefill: a chunk attends to its cached prefix and to itself
  *     (Mini-SGLang 源码解析（二）, sections 6.6 and 6.9; "推理运行时", section Prefill 与 decode 输入);
- *   - a quantized cache keeps K/V as int8 instead of bf16, at some loss of accuracy
- *     ("LLM Infra 101 v0.2: KV Cache", inference-engine list, KV Quantization). The pages fix no
- *     scheme; the one restated here is symmetric, one scale per (token, kv head) row.
+ *   - a quantized cache keeps K/V as int8 (or another 8-bit type) instead of bf16, at some loss of
+ *     accuracy ("LLM Infra 101 v0.2: KV Cache", inference-engine list, KV Quantization). The pages fix no
+ *     scheme; the ones restated here are symmetric, one scale per (token, kv head) row, with int8 codes
+ *     or OCP float8 E4M3 codes.
  * Attention itself is the textbook definition softmax(scale * q . k) weighted sum of v.
  */
 #include <math.h>
@@ -179,6 +181,117 @@ int orc_dequantize_int8(const int8_t *codes, const float *scales, int64_t nrows,
     if (nrows < 0 || dim <= 0) return fail("bad sizes (rows %lld, dim %d)", (long long)nrows, dim);
     for (int64_t r = 0; r < nrows; ++r)
         for (int32_t d = 0; d < dim; ++d) out[r * dim + d] = (double)codes[r * dim + d] * (double)scales[r];
+    return ORC_OK;
+}
+
+/*
+ * float8 E4M3 of the OCP 8-bit floating point format: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+ * bits; exponent field 0 holds the subnormals (m / 8) * 2^-6; the pattern with every exponent and mantissa
+ * bit set is NaN and there are no infinities, so finite magnitudes end at 1.75 * 2^8 = 448.
+ * orc_e4m3_value: the value of a code (NaN for the two NaN patterns).
+ */
+double orc_e4m3_value(int code) {
+    int sign = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    double mag = e == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/*
+ * orc_e4m3_encode: v rounded to the E4M3 grid, to nearest with a tie going to the even mantissa; past the
+ * largest finite value the grid continues with 480 (where the NaN pattern sits), so |v| <= 464 rounds to at
+ * most 448 and |v| > 464 gives NaN. The sign bit is v's (-0.0 and small negatives give 0x80). Codes
+ * 0x00 .. 0x7e are the non-negative finite values in increasing order; the nearest is found by bisection.
+ * v must not be NaN.
+ */
+int orc_e4m3_encode(float v) {
+    double a = fabs((double)v);
+    int sign = signbit(v) ? 0x80 : 0;
+    if (a > 464.0) return sign | 0x7f;
+    if (a >= orc_e4m3_value(0x7e)) return sign | 0x7e;
+    int lo = 0, hi = 0x7e;                    /* value(lo) <= a < value(hi) */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (orc_e4m3_value(mid) <= a) lo = mid;
+        else hi = mid;
+    }
+    double dl = a - orc_e4m3_value(lo), dh = orc_e4m3_value(hi) - a;
+    int c = dl < dh ? lo : dh < dl ? hi : ((lo & 1) ? hi : lo);
+    return sign | c;
+}
+
+/*
+ * fp8 quantization of rows of `dim` elements, one scale per row, all arithmetic in float32:
+ *   a = max_d |x_d|,  scale = a / 448,  code_d = orc_e4m3_encode(x_d / scale);
+ * a row of zeros gets scale 0 and codes 0. |x_d / scale| <= 448 up to one rounding, so no code is NaN.
+ * Dequantized, x_d ~ e4m3_value(code_d) * scale, |error| <= 2^-4 |x_d| (normal codes) or 2^-10 scale.
+ * Rows must be finite.
+ */
+int orc_quantize_fp8(int dtype, const void *rows, int64_t nrows, int32_t dim, uint8_t *codes, float *scales) {
+    if (dtype != 0 && dtype != 1) return fail("bad dtype %d", dtype);
+    if (nrows < 0 || dim <= 0) return fail("bad sizes (rows %lld, dim %d)", (long long)nrows, dim);
+    for (int64_t r = 0; r < nrows; ++r) {
+        float a = 0.0f;
+        for (int32_t d = 0; d < dim; ++d) {
+            float x = (float)elem(dtype, rows, r * dim + d);
+            if (!isfinite(x)) return fail("row %lld holds a non-finite value", (long long)r);
+            if (fabsf(x) > a) a = fabsf(x);
+        }
+        float scale = a / 448.0f;
+        scales[r] = scale;
+        for (int32_t d = 0; d < dim; ++d) {
+            int code = 0;
+            if (a > 0.0f) {
+                float x = (float)elem(dtype, rows, r * dim + d);
+                code = orc_e4m3_encode(x / scale);
+            }
+            codes[r * dim + d] = (uint8_t)code;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Store into an fp8 cache, exactly as orc_store_int8 with orc_quantize_fp8 codes. */
+int orc_store_fp8(int dtype, const void *key, const void *value, uint8_t *key_cache, uint8_t *value_cache,
+                  float *key_scale, float *value_scale, const int32_t *slot_mapping, int64_t num_tokens,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks) {
+    if (dtype != 0 && dtype != 1) return fail("bad dtype %d", dtype);
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
+        return fail("bad sizes (tokens %lld, blocks %lld)", (long long)num_tokens, (long long)num_blocks);
+    int64_t nslots = num_blocks * block_size;
+    unsigned char *seen = (unsigned char *)calloc((size_t)(nslots > 0 ? nslots : 1), 1);
+    if (!seen) return fail("out of memory");
+    for (int64_t n = 0; n < num_tokens; ++n) {
+        int64_t s = slot_mapping[n];
+        if (s < 0) continue;
+        if (s >= nslots) { free(seen); return fail("slot %lld outside the pool of %lld slots", (long long)s, (long long)nslots); }
+        if (seen[s]) { free(seen); return fail("slot %lld written twice (token %lld)", (long long)s, (long long)n); }
+        seen[s] = 1;
+    }
+    free(seen);
+    size_t eb = elem_bytes(dtype);
+    for (int64_t n = 0; n < num_tokens; ++n) {
+        int64_t s = slot_mapping[n];
+        if (s < 0) continue;
+        int64_t block = s / block_size, off = s % block_size;
+        for (int64_t h = 0; h < num_kv_heads; ++h) {
+            int64_t row = (block * num_kv_heads + h) * block_size + off;
+            int64_t src = (n * num_kv_heads + h) * head_dim;
+            int rc = orc_quantize_fp8(dtype, (const char *)key + src * eb, 1, head_dim, key_cache + row * head_dim,
+                                      key_scale + row);
+            if (!rc) rc = orc_quantize_fp8(dtype, (const char *)value + src * eb, 1, head_dim,
+                                           value_cache + row * head_dim, value_scale + row);
+            if (rc) return rc;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Dequantize fp8 rows: out[r][d] = e4m3_value(codes[r][d]) * scales[r] in float64 (exact). */
+int orc_dequantize_fp8(const uint8_t *codes, const float *scales, int64_t nrows, int32_t dim, double *out) {
+    if (nrows < 0 || dim <= 0) return fail("bad sizes (rows %lld, dim %d)", (long long)nrows, dim);
+    for (int64_t r = 0; r < nrows; ++r)
+        for (int32_t d = 0; d < dim; ++d) out[r * dim + d] = orc_e4m3_value(codes[r * dim + d]) * (double)scales[r];
     return ORC_OK;
 }
 

@@ -15,7 +15,11 @@ What pins what:
   last row of causal prefill, chunk-split invariance;
 * int8 cache quantization: exact cases (power-of-two scales), round-half-even ties, the half-step error
   bound, sign symmetry, placement by slot, and decode on an exactly quantized cache equal to decode on
-  the float cache.
+  the float cache;
+* fp8 (OCP float8 E4M3) cache quantization: the format's fixed points (zero, the smallest subnormal and
+  normal, one, 448, the NaN patterns), its grid structure, encoding and decoding of every code against
+  torch's own ``float8_e4m3fn`` conversion (round half to even, NaN past 464), the relative error bound,
+  placement by slot, and decode on an exactly representable cache equal to decode on the float cache.
 """
 from __future__ import annotations
 
@@ -366,6 +370,118 @@ def check_int8_decode_exact_case_matches_float_decode(orc, seed=53):
     assert np.abs(got - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
 
 
+def check_e4m3_fixed_points_and_grid(orc):
+    """Values the E4M3 format fixes: 0x00 = 0, 0x80 = -0, 0x01 = 2^-9 (smallest subnormal), 0x08 = 2^-6
+    (smallest normal), 0x38 = 1, 0x40 = 2, 0x7e = 448 (largest finite), 0x7f and 0xff NaN. The non-negative
+    finite codes increase; within the subnormals and the first binade the step is 2^-9; each further binade of
+    8 codes doubles the one before; negative codes mirror positive ones."""
+    v = [orc.e4m3_value(c) for c in range(256)]
+    assert v[0x00] == 0.0 and not math.copysign(1.0, v[0x00]) < 0
+    assert v[0x80] == 0.0 and math.copysign(1.0, v[0x80]) < 0
+    assert v[0x01] == 2.0 ** -9 and v[0x08] == 2.0 ** -6 and v[0x38] == 1.0 and v[0x40] == 2.0 and v[0x7e] == 448.0
+    assert math.isnan(v[0x7f]) and math.isnan(v[0xff])
+    assert all(v[c + 1] > v[c] for c in range(0x7e))
+    assert all(v[c + 1] - v[c] == 2.0 ** -9 for c in range(16))
+    assert all(v[c + 8] == 2 * v[c] for c in range(8, 0x77))
+    assert all(v[c | 0x80] == -v[c] for c in range(0x7f))
+
+
+def check_e4m3_matches_torch(orc, seed=54):
+    """Decoding of every code, and encoding of random floats (six decades, both signs), of every code's value,
+    of every midpoint between neighbouring codes (ties), of points just off the midpoints, and of values
+    around the top of the range, against torch's float8_e4m3fn conversion on the CPU."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    tv = codes.view(torch.float8_e4m3fn).double().numpy()
+    ov = np.array([orc.e4m3_value(c) for c in range(256)])
+    assert np.array_equal(np.isnan(tv), np.isnan(ov))
+    fin = ~np.isnan(tv)
+    assert np.array_equal(tv[fin], ov[fin]) and np.array_equal(np.signbit(tv[fin]), np.signbit(ov[fin]))
+    rng = np.random.default_rng(seed)
+    pos = np.array([orc.e4m3_value(c) for c in range(0x7f)])
+    mids = (pos[:-1] + pos[1:]) / 2
+    xs = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.uniform(-4, 2.6, 4000), pos, -pos, mids, -mids,
+                         np.nextafter(mids, 0), np.nextafter(mids, 1e9), [448.0, 455.0, 463.99, 464.0, 464.01, 470.0,
+                                                                          -464.0, -470.0, 1e-9, -1e-9, 0.0, -0.0]])
+    xs = xs.astype(np.float32)
+    want = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.int64)
+    got = np.array([orc.e4m3_encode(x) for x in xs], np.int64)
+    assert np.array_equal(got, want)
+
+
+def check_fp8_zero_row_bound_and_symmetry(orc, seed=55):
+    """A zero row gives scale 0 and codes 0. Random rows: scale = max|x| / 448, the largest magnitude maps to
+    +-448, |e4m3(code) * scale - x| <= 2^-4 |x| where x / scale is at least 2^-6 (normal codes) and
+    <= 2^-10 scale below, and negating a row flips the sign bits with the same scale."""
+    rng = np.random.default_rng(seed)
+    z_codes, z_scales = orc.quantize_fp8(F32, np.zeros((1, 16), np.float32))
+    assert z_scales[0] == 0.0 and not z_codes.any()
+    x = (rng.standard_normal((40, 64)) * rng.uniform(0.01, 100, (40, 1))).astype(np.float32)
+    x[3, :8] = 1e-4 * x[3, 8]                      # entries deep in the subnormal range of the row
+    codes, scales = orc.quantize_fp8(F32, x)
+    a = np.abs(x).max(axis=1)
+    assert np.array_equal(scales, (a / np.float32(448.0)).astype(np.float32))
+    deq = orc.dequantize_fp8(codes, scales)
+    err = np.abs(deq - x.astype(np.float64))
+    sc = scales[:, None].astype(np.float64)
+    normal = np.abs(x) >= 2.0 ** -6 * sc
+    assert np.all(err[normal] <= 2.0 ** -4 * np.abs(x.astype(np.float64))[normal] * (1 + 1e-6))
+    assert np.all(err[~normal] <= 2.0 ** -10 * np.broadcast_to(sc, x.shape)[~normal] * (1 + 1e-6))
+    i = np.argmax(np.abs(x), axis=1)
+    assert np.array_equal(codes[np.arange(40), i] & 0x7f, np.full(40, 0x7e))
+    n_codes, n_scales = orc.quantize_fp8(F32, -x)
+    assert np.array_equal(n_scales, scales) and np.array_equal(n_codes, codes ^ 0x80)
+
+
+def check_fp8_store_places_rows(orc, seed=56):
+    """store_fp8 puts each row's codes and scale at (s // bs, head, s % bs) of the [NB, Hkv, bs(, D)]
+    arrays; untouched rows keep their sentinels; negative slots write nothing."""
+    rng = np.random.default_rng(seed)
+    nb, hkv, bs, d = 5, 2, 4, 8
+    kc = np.full((nb, hkv, bs, d), 99, np.uint8)
+    vc = np.full((nb, hkv, bs, d), 199, np.uint8)
+    ks = np.full((nb, hkv, bs), -1.0, np.float32)
+    vs = np.full((nb, hkv, bs), -2.0, np.float32)
+    slots = np.array([3, 17, -1, 8, 19], np.int32)
+    key = rng.standard_normal((5, hkv, d)).astype(np.float32)
+    val = (3 * rng.standard_normal((5, hkv, d))).astype(np.float32)
+    orc.store_fp8(F32, key, val, kc, vc, ks, vs, slots)
+    touched = np.zeros((nb, bs), bool)
+    for n, s in enumerate(slots):
+        if s < 0:
+            continue
+        for h in range(hkv):
+            kq, ksc = orc.quantize_fp8(F32, key[n, h][None])
+            vq, vsc = orc.quantize_fp8(F32, val[n, h][None])
+            assert np.array_equal(kc[s // bs, h, s % bs], kq[0]) and ks[s // bs, h, s % bs] == ksc[0]
+            assert np.array_equal(vc[s // bs, h, s % bs], vq[0]) and vs[s // bs, h, s % bs] == vsc[0]
+        touched[s // bs, s % bs] = True
+    assert np.all(kc.transpose(0, 2, 1, 3)[~touched] == 99) and np.all(vc.transpose(0, 2, 1, 3)[~touched] == 199)
+    assert np.all(ks.transpose(0, 2, 1)[~touched] == -1.0) and np.all(vs.transpose(0, 2, 1)[~touched] == -2.0)
+
+
+def check_fp8_decode_exact_case_matches_float_decode(orc, seed=57):
+    """Rows whose elements are E4M3 values times a power of two, with one element at +-448 times it: the
+    quantization is exact, so decode over the dequantized fp8 cache ("f64") equals decode over the float
+    cache."""
+    rng = np.random.default_rng(seed)
+    nb, hkv, bs, d = 8, 2, 4, 8
+    grid = np.array([orc.e4m3_value(c) for c in range(0x7f)])
+    pick = grid[rng.integers(0, 0x7f, size=(nb, hkv, bs, d))] * np.where(rng.random((nb, hkv, bs, d)) < 0.5, 1, -1)
+    pick[..., 0] = np.where(rng.random((nb, hkv, bs)) < 0.5, 448.0, -448.0)
+    kf = (pick * 0.25).astype(np.float32)
+    vf = (np.roll(pick, 1, axis=-1) * 2.0 ** -10).astype(np.float32)
+    kq, ks = orc.quantize_fp8(F32, kf)
+    vq, vs = orc.quantize_fp8(F32, vf)
+    assert np.array_equal(orc.dequantize_fp8(kq, ks), kf.astype(np.float64))
+    bt = _tables(rng, [13, 5], bs, nb)
+    q = rng.standard_normal((2, 4, d)).astype(np.float32)
+    lens = np.array([13, 5], np.int32)
+    ref = orc.decode(F32, q, kf, vf, bt, lens, 0.01)
+    got = orc.decode("f64", q.astype(np.float64), orc.dequantize_fp8(kq, ks), orc.dequantize_fp8(vq, vs), bt, lens,
+                     0.01)
+    assert np.abs(got - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
 ALL_CHECKS = [
     check_gather_matches_numpy_indexing,
     check_single_key,
@@ -385,4 +501,9 @@ ALL_CHECKS = [
     check_int8_zero_row_bound_and_symmetry,
     check_int8_store_places_rows,
     check_int8_decode_exact_case_matches_float_decode,
+    check_e4m3_fixed_points_and_grid,
+    check_e4m3_matches_torch,
+    check_fp8_zero_row_bound_and_symmetry,
+    check_fp8_store_places_rows,
+    check_fp8_decode_exact_case_matches_float_decode,
 ]

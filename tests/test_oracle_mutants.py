@@ -65,6 +65,12 @@ MUTANTS = {
     "int8_dequant_drops_scale": ("(double)codes[r * dim + d] * (double)scales[r];", "(double)codes[r * dim + d];"),
     "int8_store_scale_at_offset": ("key_cache + row * head_dim,\n                                       key_scale + row);",
                                    "key_cache + row * head_dim,\n                                       key_scale + off);"),
+    "fp8_exponent_bias_8": ("ldexp(1.0 + m / 8.0, e - 7);", "ldexp(1.0 + m / 8.0, e - 8);"),
+    "fp8_subnormal_exponent": ("ldexp(m / 8.0, -6)", "ldexp(m / 8.0, -7)"),
+    "fp8_ties_go_up": ("((lo & 1) ? hi : lo);", "hi;"),
+    "fp8_scale_over_240": ("float scale = a / 448.0f;", "float scale = a / 240.0f;"),
+    "fp8_dequant_drops_scale": ("orc_e4m3_value(codes[r * dim + d]) * (double)scales[r];",
+                                "orc_e4m3_value(codes[r * dim + d]);"),
 }
 
 
