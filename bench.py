@@ -12,7 +12,7 @@ R * step bytes >> the last-level cache), so K/V come from HBM, not from cache.
 Prints one JSON line (rank 0): value = algorithmic bytes of the step / step time (GB/s), plus the
 roofline of the decode call measured with HIP events on the launch stream, and the CPU oracle's rate
 on a bounded sample of the same workload. Secondary legs (not part of `value`): the same decode over
-an int8 cache, and the chunked-prefill workload on MFMA.
+an int8 and over an fp8 (E4M3) cache, and the chunked-prefill workload on MFMA.
 """
 from __future__ import annotations
 
@@ -42,18 +42,28 @@ def decode_bytes(c) -> int:
                + 4 * nb.sum() + 4 * c.num_seqs)
 
 
-def decode_bytes_int8(c) -> int:
-    """Algorithmic bytes of one decode call over an int8 cache: the int8 codes of K and V of every context
-    token, their fp32 row scales, q and out (bf16), the block-table entries used and context_lens."""
+def decode_bytes_q8(c) -> int:
+    """Algorithmic bytes of one decode call over an 8-bit cache (int8 or fp8 codes): the one-byte codes of K
+    and V of every context token, their fp32 row scales, q and out (bf16), the block-table entries used and
+    context_lens."""
     lens = c.context_lens.astype(np.int64)
     nb = -(-lens // c.block_size)
     return int(2 * lens.sum() * c.num_kv_heads * (c.head_dim + 4) + 2 * c.num_seqs * c.num_heads * c.head_dim * 2
                + 4 * nb.sum() + 4 * c.num_seqs)
 
 
-def bench_int8(pkv, torch, W, c, dev, copies, steps, warmup):
-    """The same decode workload over an int8 cache (rows quantized by kv_cache_store_int8 from the bf16
+Q8_LEGS = {
+    "int8": ("int8 codes + fp32 scale per (token, kv head) row", "kv_cache_store_int8", "paged_attention_decode_int8"),
+    "fp8": ("float8 E4M3 codes + fp32 scale per (token, kv head) row", "kv_cache_store_fp8",
+            "paged_attention_decode_fp8"),
+}
+
+
+def bench_q8(kind, pkv, torch, W, c, dev, copies, steps, warmup):
+    """The same decode workload over an 8-bit cache (rows quantized by the library's store from the bf16
     values; pool copies rotated as in the main leg): average decode-call time from HIP events."""
+    what, store_name, decode_name = Q8_LEGS[kind]
+    store, decode = getattr(pkv, store_name), getattr(pkv, decode_name)
     kr, vr, slots = W.cached_rows(c.pool)
 
     def tt(a):
@@ -63,12 +73,12 @@ def bench_int8(pkv, torch, W, c, dev, copies, steps, warmup):
     shape = (c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
     pools = []
     for _ in range(copies):
-        kc = torch.zeros(shape, dtype=torch.int8, device=dev)
+        kc = torch.zeros(shape, dtype=torch.int8 if kind == "int8" else torch.uint8, device=dev)
         vc = torch.zeros_like(kc)
         ks = torch.zeros(shape[:3], dtype=torch.float32, device=dev)
         vs = torch.zeros_like(ks)
-        pkv.kv_cache_store_int8(kr, vr, kc, vc, ks, vs, slots)
-        pkv.kv_cache_store_int8(tt(c.key), tt(c.value), kc, vc, ks, vs, torch.from_numpy(c.slot_mapping).to(dev))
+        store(kr, vr, kc, vc, ks, vs, slots)
+        store(tt(c.key), tt(c.value), kc, vc, ks, vs, torch.from_numpy(c.slot_mapping).to(dev))
         pools.append((kc, vc, ks, vs))
     q = tt(c.query)
     out = torch.empty_like(q)
@@ -82,14 +92,13 @@ def bench_int8(pkv, torch, W, c, dev, copies, steps, warmup):
         kc, vc, ks, vs = pools[k % copies]
         if k >= warmup:
             ev[k - warmup][0].record(stream)
-        pkv.paged_attention_decode_int8(out, q, kc, vc, ks, vs, bt, cl, c.max_context_len, c.scale, workspace=ws,
-                                        stream=stream)
+        decode(out, q, kc, vc, ks, vs, bt, cl, c.max_context_len, c.scale, workspace=ws, stream=stream)
         if k >= warmup:
             ev[k - warmup][1].record(stream)
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    nbytes = decode_bytes_int8(c)
-    return {"workload": c.name, "cache": "int8 codes + fp32 scale per (token, kv head) row",
+    nbytes = decode_bytes_q8(c)
+    return {"workload": c.name, "cache": what,
             "decode_ms": round(ms, 5), "algorithmic_bytes": nbytes,
             "achieved_gbs": round(nbytes / (ms * 1e-3) / 1e9, 2),
             "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -224,7 +233,7 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="pool copies rotated per step (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
-    ap.add_argument("--no-int8", action="store_true", help="skip the int8-cache decode leg")
+    ap.add_argument("--no-int8", action="store_true", help="skip the 8-bit-cache (int8, fp8) decode legs")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -334,9 +343,11 @@ def main():
         "torch": torch.__version__,
     }
     if c.dtype == "bf16" and c.head_dim == 128 and c.block_size >= 16 and not args.no_int8:
-        del pools
-        result["int8_cache"] = bench_int8(pkv, torch, W, c, dev, copies, args.steps, args.warmup)
-        result["int8_cache"]["speedup_vs_bf16_cache"] = round(dec_avg_ms / result["int8_cache"]["decode_ms"], 3)
+        pools = None
+        for kind in ("int8", "fp8"):
+            leg = bench_q8(kind, pkv, torch, W, c, dev, copies, args.steps, args.warmup)
+            leg["speedup_vs_bf16_cache"] = round(dec_avg_ms / leg["decode_ms"], 3)
+            result[f"{kind}_cache"] = leg
     if not args.no_prefill:
         pools = None
         result["prefill"] = bench_prefill(pkv, torch, dev)

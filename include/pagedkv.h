@@ -8,7 +8,8 @@
  *                               cached prefix plus the chunk;
  *   pkv_kv_cache_gather         inverse of the store for one block table (test helper);
  *   pkv_kv_cache_copy_blocks    copy whole blocks (copy-on-write of shared blocks);
- *   pkv_kv_cache_store_int8, pkv_paged_attention_decode_int8: the same over an int8 cache.
+ *   pkv_kv_cache_store_int8, pkv_paged_attention_decode_int8: the same over an int8 cache;
+ *   pkv_kv_cache_store_fp8, pkv_paged_attention_decode_fp8: the same over an fp8 (E4M3) cache.
  *
  * Vocabulary (nano-vllm walkthrough, section 2 context: is_prefill, cu_seqlens_q/k, max_seqlen_q/k,
  * slot_mapping, context_lens, block_tables; "推理运行时", section 分页 KV: logical block j of a
@@ -198,6 +199,38 @@ pkv_status pkv_paged_attention_decode_int8(pkv_dtype dtype, void *out, const voi
                                            int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
                                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fp8 KV cache (same source: an 8-bit cache instead of bf16). The pages name no 8-bit float format; this
+ * library uses OCP float8 E4M3, the element type of gfx950's fp8 conversions: 1 sign bit, 4 exponent bits
+ * (bias 7), 3 mantissa bits, subnormals (m / 8) * 2^-6, no infinities, NaN only for S.1111.111, largest
+ * finite magnitude 448. One fp32 scale per (token, kv head) row:
+ *   scale = max_d |x_d| / 448,  code_d = E4M3(x_d / scale), rounded to nearest, ties to even,
+ * in fp32 with IEEE division (a row of zeros: scale 0, codes 0); |x_d / scale| <= 448 up to one rounding,
+ * so no code is NaN. Dequantized, x_d ~ value(code_d) * scale with |error| <= 2^-4 |x_d| where
+ * |x_d / scale| >= 2^-6, else <= 2^-10 scale.
+ *   key_cache, value_cache  uint8 codes [num_blocks][num_kv_heads][block_size][head_dim];
+ *   key_scale, value_scale  fp32 [num_blocks][num_kv_heads][block_size], one per cache row.
+ */
+
+/* kv_cache_store_fp8: pkv_kv_cache_store_int8 with E4M3 codes as above (same arguments, alignment, errors). */
+pkv_status pkv_kv_cache_store_fp8(pkv_dtype dtype, const void *key, const void *value, uint8_t *key_cache,
+                                  uint8_t *value_cache, float *key_scale, float *value_scale,
+                                  const int32_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int64_t num_blocks, hipStream_t stream);
+
+/*
+ * paged_attention_decode_fp8: pkv_paged_attention_decode_int8 over an fp8 cache: attention over the
+ * dequantized K/V (value(code) * scale), with the same restrictions (bf16 query and out, head_dim 128,
+ * block_size >= 16), precision and workspace. The codes become exact bf16 values on the GPU.
+ */
+pkv_status pkv_paged_attention_decode_fp8(pkv_dtype dtype, void *out, const void *query, const uint8_t *key_cache,
+                                          const uint8_t *value_cache, const float *key_scale,
+                                          const float *value_scale, const int32_t *block_tables,
+                                          int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
+                                          int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Message of the calling thread's last non-OK status ("" if none). Owned by the library. */
 const char *pkv_last_error(void);

@@ -50,6 +50,9 @@ def load_library(path: str = LIB_PATH):
         "pkv_kv_cache_store_int8": [ctypes.c_int, P, P, P, P, P, P, P, I64, I32, I32, I32, I64, P],
         "pkv_paged_attention_decode_int8": [ctypes.c_int, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32,
                                             I64, F, P, SZ, P],
+        "pkv_kv_cache_store_fp8": [ctypes.c_int, P, P, P, P, P, P, P, I64, I32, I32, I32, I64, P],
+        "pkv_paged_attention_decode_fp8": [ctypes.c_int, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32,
+                                           I64, F, P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -193,10 +196,10 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
                                           _ptr(workspace), ws_bytes, _stream(stream)))
 
 
-def kv_cache_store_int8(key, value, key_cache, value_cache, key_scale, value_scale, slot_mapping, stream=None):
-    """Quantize ``key``/``value`` [N, Hkv, D] (bf16 or fp32) row by row and scatter the int8 codes into
-    ``key_cache``/``value_cache`` int8 [NB, Hkv, bs, D] and the fp32 row scales into ``key_scale``/
-    ``value_scale`` [NB, Hkv, bs] at the slots ``slot_mapping`` (int32 [N]; negative = skip)."""
+_CODE_DTYPES = {"int8": (torch.int8,), "fp8": (torch.uint8, torch.float8_e4m3fn)}
+
+
+def _store_q8(kind, key, value, key_cache, value_cache, key_scale, value_scale, slot_mapping, stream):
     lib = load_library()
     _dev(key, value, key_cache, value_cache, key_scale, value_scale, slot_mapping)
     _i32(slot_mapping)
@@ -206,21 +209,19 @@ def kv_cache_store_int8(key, value, key_cache, value_cache, key_scale, value_sca
         raise ValueError("key/value must be [N, Hkv, D] and both caches [NB, Hkv, bs, D]")
     if key_scale.shape != (nb, hkv, bs) or value_scale.shape != (nb, hkv, bs):
         raise ValueError("scales must be [NB, Hkv, bs]")
-    if key_cache.dtype != torch.int8 or value_cache.dtype != torch.int8:
-        raise ValueError("int8 caches expected")
+    if key_cache.dtype not in _CODE_DTYPES[kind] or value_cache.dtype not in _CODE_DTYPES[kind]:
+        raise ValueError(f"{kind} caches expected ({', '.join(str(t) for t in _CODE_DTYPES[kind])})")
     if key_scale.dtype != torch.float32 or value_scale.dtype != torch.float32:
         raise ValueError("float32 scales expected")
     if slot_mapping.shape != (n,) or key.dtype != value.dtype:
         raise ValueError("slot_mapping must have one entry per token; key and value share a dtype")
-    _check(lib.pkv_kv_cache_store_int8(_dtype_code(key), _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
-                                       _ptr(key_scale), _ptr(value_scale), _ptr(slot_mapping), n, hkv, d, bs, nb,
-                                       _stream(stream)))
+    fn = lib.pkv_kv_cache_store_int8 if kind == "int8" else lib.pkv_kv_cache_store_fp8
+    _check(fn(_dtype_code(key), _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(key_scale),
+              _ptr(value_scale), _ptr(slot_mapping), n, hkv, d, bs, nb, _stream(stream)))
 
 
-def paged_attention_decode_int8(out, query, key_cache, value_cache, key_scale, value_scale, block_tables,
-                                context_lens, max_context_len, scale, workspace=None, stream=None):
-    """Decode attention over an int8 cache (codes [NB, Hkv, bs, D], fp32 scales [NB, Hkv, bs]); bf16
-    ``out``/``query`` [B, Hq, D], D = 128, block size >= 16. Workspace as for ``paged_attention_decode``."""
+def _decode_q8(kind, out, query, key_cache, value_cache, key_scale, value_scale, block_tables, context_lens,
+               max_context_len, scale, workspace, stream):
     lib = load_library()
     _dev(out, query, key_cache, value_cache, key_scale, value_scale, block_tables, context_lens, workspace)
     _i32(block_tables, context_lens)
@@ -230,20 +231,47 @@ def paged_attention_decode_int8(out, query, key_cache, value_cache, key_scale, v
         raise ValueError("query/out must be [B, Hq, D] with the caches' D")
     if key_scale.shape != (nb, hkv, bs) or value_scale.shape != (nb, hkv, bs):
         raise ValueError("scales must be [NB, Hkv, bs]")
-    if key_cache.dtype != torch.int8 or value_cache.dtype != torch.int8 or key_scale.dtype != torch.float32 \
-            or value_scale.dtype != torch.float32:
-        raise ValueError("int8 caches and float32 scales expected")
+    if key_cache.dtype not in _CODE_DTYPES[kind] or value_cache.dtype not in _CODE_DTYPES[kind] \
+            or key_scale.dtype != torch.float32 or value_scale.dtype != torch.float32:
+        raise ValueError(f"{kind} caches and float32 scales expected")
     if block_tables.dim() != 2 or block_tables.shape[0] != b or context_lens.shape != (b,):
         raise ValueError("block_tables must be [B, stride] and context_lens [B]")
     ws_need = decode_workspace_size(b, hq, hkv, d, bs, max_context_len)
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=query.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.pkv_paged_attention_decode_int8(_dtype_code(query), _ptr(out), _ptr(query), _ptr(key_cache),
-                                               _ptr(value_cache), _ptr(key_scale), _ptr(value_scale),
-                                               _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), b,
-                                               int(max_context_len), hq, hkv, d, bs, nb, float(scale),
-                                               _ptr(workspace), ws_bytes, _stream(stream)))
+    fn = lib.pkv_paged_attention_decode_int8 if kind == "int8" else lib.pkv_paged_attention_decode_fp8
+    _check(fn(_dtype_code(query), _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(key_scale),
+              _ptr(value_scale), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), b,
+              int(max_context_len), hq, hkv, d, bs, nb, float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kv_cache_store_int8(key, value, key_cache, value_cache, key_scale, value_scale, slot_mapping, stream=None):
+    """Quantize ``key``/``value`` [N, Hkv, D] (bf16 or fp32) row by row and scatter the int8 codes into
+    ``key_cache``/``value_cache`` int8 [NB, Hkv, bs, D] and the fp32 row scales into ``key_scale``/
+    ``value_scale`` [NB, Hkv, bs] at the slots ``slot_mapping`` (int32 [N]; negative = skip)."""
+    _store_q8("int8", key, value, key_cache, value_cache, key_scale, value_scale, slot_mapping, stream)
+
+
+def paged_attention_decode_int8(out, query, key_cache, value_cache, key_scale, value_scale, block_tables,
+                                context_lens, max_context_len, scale, workspace=None, stream=None):
+    """Decode attention over an int8 cache (codes [NB, Hkv, bs, D], fp32 scales [NB, Hkv, bs]); bf16
+    ``out``/``query`` [B, Hq, D], D = 128, block size >= 16. Workspace as for ``paged_attention_decode``."""
+    _decode_q8("int8", out, query, key_cache, value_cache, key_scale, value_scale, block_tables, context_lens,
+               max_context_len, scale, workspace, stream)
+
+
+def kv_cache_store_fp8(key, value, key_cache, value_cache, key_scale, value_scale, slot_mapping, stream=None):
+    """``kv_cache_store_int8`` with OCP float8 E4M3 codes (scale max|x| / 448, round half to even); the caches
+    hold the code bytes as uint8 (or torch.float8_e4m3fn) [NB, Hkv, bs, D]."""
+    _store_q8("fp8", key, value, key_cache, value_cache, key_scale, value_scale, slot_mapping, stream)
+
+
+def paged_attention_decode_fp8(out, query, key_cache, value_cache, key_scale, value_scale, block_tables,
+                               context_lens, max_context_len, scale, workspace=None, stream=None):
+    """Decode attention over an fp8 (E4M3) cache; otherwise as ``paged_attention_decode_int8``."""
+    _decode_q8("fp8", out, query, key_cache, value_cache, key_scale, value_scale, block_tables, context_lens,
+               max_context_len, scale, workspace, stream)
 
 
 def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, cu_seqlens_q, cu_seqlens_k,

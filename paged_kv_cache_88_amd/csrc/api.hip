@@ -271,7 +271,7 @@ pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *qu
                                       int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
                                       int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
                                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    pkv::DecodeArgs a;
+    pkv::DecodeArgs a{};
     pkv_status st = decode_args(a, dtype, out, query, key_cache, value_cache, block_tables,
                                 block_table_stride, context_lens, num_seqs, max_context_len, num_heads, num_kv_heads,
                                 head_dim, block_size, num_blocks, scale, workspace, workspace_bytes);
@@ -280,10 +280,16 @@ pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *qu
                       "paged_attention_decode launch");
 }
 
-pkv_status pkv_kv_cache_store_int8(pkv_dtype dtype, const void *key, const void *value, int8_t *key_cache,
-                                   int8_t *value_cache, float *key_scale, float *value_scale,
-                                   const int32_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
-                                   int32_t head_dim, int32_t block_size, int64_t num_blocks, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared bodies of the int8 and fp8 entry points (the same layouts, checks and kernels; only the code type
+// differs).
+pkv_status store_q8(bool fp8, const char *what, pkv_dtype dtype, const void *key, const void *value,
+                    void *key_cache, void *value_cache, float *key_scale, float *value_scale,
+                    const int32_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int64_t num_blocks, hipStream_t stream) {
     pkv_status st = check_common(dtype, num_kv_heads, head_dim, block_size, num_blocks);
     if (st != PKV_OK) return st;
     REQUIRE(num_tokens >= 0, PKV_EINVAL, "num_tokens must be non-negative (got %lld)", (long long)num_tokens);
@@ -294,23 +300,22 @@ pkv_status pkv_kv_cache_store_int8(pkv_dtype dtype, const void *key, const void 
                 ((uintptr_t)key_scale & 3u) == 0 && ((uintptr_t)value_scale & 3u) == 0,
             PKV_EINVAL, "key, value and cache pointers must be 16-byte aligned, scales 4-byte aligned");
     REQUIRE(num_tokens * num_kv_heads <= (int64_t)1 << 40, PKV_EINVAL, "num_tokens too large");
-    return hip_status(pkv::launch_store_int8(dtype == PKV_BF16, head_dim, key, value, key_cache, value_cache, key_scale,
-                                             value_scale, slot_mapping, num_tokens, num_kv_heads, block_size,
-                                             (int)num_blocks, stream),
-                      "kv_cache_store_int8 launch");
+    return hip_status(pkv::launch_store_q8(dtype == PKV_BF16, fp8, head_dim, key, value, key_cache, value_cache,
+                                           key_scale, value_scale, slot_mapping, num_tokens, num_kv_heads, block_size,
+                                           (int)num_blocks, stream),
+                      what);
 }
 
-pkv_status pkv_paged_attention_decode_int8(pkv_dtype dtype, void *out, const void *query, const int8_t *key_cache,
-                                           const int8_t *value_cache, const float *key_scale,
-                                           const float *value_scale, const int32_t *block_tables,
-                                           int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
-                                           int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
-                                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
-                                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    REQUIRE(dtype == PKV_BF16, PKV_EUNSUPPORTED, "int8-cache decode takes a bf16 query (got dtype %d)", (int)dtype);
-    REQUIRE(head_dim == 128, PKV_EUNSUPPORTED, "int8-cache decode supports head_dim 128 (got %d)", head_dim);
-    REQUIRE(block_size >= 16, PKV_EUNSUPPORTED, "int8-cache decode needs block_size >= 16 (got %d)", block_size);
-    pkv::DecodeArgs a;
+pkv_status decode_q8(bool fp8, const char *what, pkv_dtype dtype, void *out, const void *query,
+                     const void *key_cache, const void *value_cache, const float *key_scale,
+                     const float *value_scale, const int32_t *block_tables, int32_t block_table_stride,
+                     const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    REQUIRE(dtype == PKV_BF16, PKV_EUNSUPPORTED, "8-bit-cache decode takes a bf16 query (got dtype %d)", (int)dtype);
+    REQUIRE(head_dim == 128, PKV_EUNSUPPORTED, "8-bit-cache decode supports head_dim 128 (got %d)", head_dim);
+    REQUIRE(block_size >= 16, PKV_EUNSUPPORTED, "8-bit-cache decode needs block_size >= 16 (got %d)", block_size);
+    pkv::DecodeArgs a{};
     pkv_status st = decode_args(a, dtype, out, query, key_cache, value_cache, block_tables, block_table_stride,
                                 context_lens, num_seqs, max_context_len, num_heads, num_kv_heads, head_dim, block_size,
                                 num_blocks, scale, workspace, workspace_bytes);
@@ -320,7 +325,54 @@ pkv_status pkv_paged_attention_decode_int8(pkv_dtype dtype, void *out, const voi
             "scale arrays must be 16-byte aligned");
     a.key_scale = key_scale;
     a.value_scale = value_scale;
-    return hip_status(pkv::launch_decode_int8(a, num_heads / num_kv_heads, stream), "paged_attention_decode_int8 launch");
+    a.fp8_codes = fp8;
+    return hip_status(pkv::launch_decode_q8(a, num_heads / num_kv_heads, stream), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_kv_cache_store_int8(pkv_dtype dtype, const void *key, const void *value, int8_t *key_cache,
+                                   int8_t *value_cache, float *key_scale, float *value_scale,
+                                   const int32_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int64_t num_blocks, hipStream_t stream) {
+    return store_q8(false, "kv_cache_store_int8 launch", dtype, key, value, key_cache, value_cache, key_scale,
+                    value_scale, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size, num_blocks, stream);
+}
+
+pkv_status pkv_paged_attention_decode_int8(pkv_dtype dtype, void *out, const void *query, const int8_t *key_cache,
+                                           const int8_t *value_cache, const float *key_scale,
+                                           const float *value_scale, const int32_t *block_tables,
+                                           int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
+                                           int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return decode_q8(false, "paged_attention_decode_int8 launch", dtype, out, query, key_cache, value_cache,
+                     key_scale, value_scale, block_tables, block_table_stride, context_lens, num_seqs,
+                     max_context_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace,
+                     workspace_bytes, stream);
+}
+
+pkv_status pkv_kv_cache_store_fp8(pkv_dtype dtype, const void *key, const void *value, uint8_t *key_cache,
+                                  uint8_t *value_cache, float *key_scale, float *value_scale,
+                                  const int32_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int64_t num_blocks, hipStream_t stream) {
+    return store_q8(true, "kv_cache_store_fp8 launch", dtype, key, value, key_cache, value_cache, key_scale,
+                    value_scale, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size, num_blocks, stream);
+}
+
+pkv_status pkv_paged_attention_decode_fp8(pkv_dtype dtype, void *out, const void *query, const uint8_t *key_cache,
+                                          const uint8_t *value_cache, const float *key_scale,
+                                          const float *value_scale, const int32_t *block_tables,
+                                          int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
+                                          int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return decode_q8(true, "paged_attention_decode_fp8 launch", dtype, out, query, key_cache, value_cache,
+                     key_scale, value_scale, block_tables, block_table_stride, context_lens, num_seqs,
+                     max_context_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace,
+                     workspace_bytes, stream);
 }
 
 pkv_status pkv_paged_attention_prefill(pkv_dtype dtype, void *out, const void *query, const void *key_cache,

@@ -574,12 +574,20 @@ struct MfmaTile<true> {
 // Block size >= 16 puts each 16-token group in one block: the block id and block base are wave-uniform
 // and lanes add 32-bit row offsets.
 //
-// int8 caches (Q8): rows hold int8 codes with one fp32 scale per (token, kv head). K codes of a lane are
-// two 16-byte loads (dims 16 b .. +16 and 64 + 16 b .. +16, the MFMA reduction order permuted to match,
-// Q loaded in the same order), V codes one 8-byte load per token; codes become exact bf16 integers in
-// registers, the K scale multiplies each score, and the V scale multiplies each weight before it is
-// rounded to bf16 (the denominator sums the unscaled weights).
-template <int G, bool Q8>
+// 8-bit caches (Q8): rows hold one-byte codes with one fp32 scale per (token, kv head): int8 integers, or
+// OCP float8 E4M3 values (F8). K codes of a lane are two 16-byte loads (dims 16 b .. +16 and 64 + 16 b .. +16,
+// the MFMA reduction order permuted to match, Q loaded in the same order), V codes one 8-byte load per
+// token; codes become exact bf16 values in registers (int8: a signed-byte conversion per code; E4M3:
+// v_cvt_scalef32_pk_bf16_fp8 with scale 1, two codes per instruction), the K scale multiplies each score,
+// and the V scale multiplies each weight before it is rounded to bf16 (the denominator sums the unscaled
+// weights).
+template <bool F8, int K>
+__device__ __forceinline__ uint32_t code_pair_to_bf16x2(uint32_t w) {
+    if constexpr (F8) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, K != 0));
+    else return i8pair_to_bf16x2(w, K);
+}
+
+template <int G, bool Q8, bool F8>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const char *__restrict__ key_cache,
                    const char *__restrict__ value_cache, const int32_t *__restrict__ block_tables, int bt_stride,
@@ -698,13 +706,13 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
                 for (int c = 0; c < 4; ++c) {
                     const u32x4 w = t.k[g][c >> 1];
                     const uint32_t w0 = (c & 1) ? w[2] : w[0], w1 = (c & 1) ? w[3] : w[1];
-                    tk[g][c] = u32x4{i8pair_to_bf16x2(w0, 0), i8pair_to_bf16x2(w0, 1), i8pair_to_bf16x2(w1, 0),
-                                     i8pair_to_bf16x2(w1, 1)};
+                    tk[g][c] = u32x4{code_pair_to_bf16x2<F8, 0>(w0), code_pair_to_bf16x2<F8, 1>(w0),
+                                     code_pair_to_bf16x2<F8, 0>(w1), code_pair_to_bf16x2<F8, 1>(w1)};
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    tv[g][i] = u32x4{i8pair_to_bf16x2(t.v[g][i][0], 0), i8pair_to_bf16x2(t.v[g][i][0], 1),
-                                     i8pair_to_bf16x2(t.v[g][i][1], 0), i8pair_to_bf16x2(t.v[g][i][1], 1)};
+                    tv[g][i] = u32x4{code_pair_to_bf16x2<F8, 0>(t.v[g][i][0]), code_pair_to_bf16x2<F8, 1>(t.v[g][i][0]),
+                                     code_pair_to_bf16x2<F8, 0>(t.v[g][i][1]), code_pair_to_bf16x2<F8, 1>(t.v[g][i][1])};
             } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) tk[g][c] = t.k[g][c];
@@ -955,7 +963,9 @@ static hipError_t launch_decode_cfg(const DecodeArgs &a, hipStream_t stream) {
         static_assert(BF16 && D == 128, "matrix-core decode: bf16, head_dim 128");
         const int64_t grid = units < a.workers ? units : a.workers;
         const bool q8 = a.key_scale != nullptr;
-        hipLaunchKernelGGL((q8 ? decode_mfma_kernel<G, true> : decode_mfma_kernel<G, false>), dim3((unsigned)grid),
+        auto kernel = !q8 ? decode_mfma_kernel<G, false, false>
+                          : a.fp8_codes ? decode_mfma_kernel<G, true, true> : decode_mfma_kernel<G, true, false>;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)grid),
                            dim3(64), 0, stream, a.out, a.query, (const char *)a.key_cache, (const char *)a.value_cache,
                            a.block_tables, a.bt_stride, a.items, a.ctrl, a.num_kv_heads, a.num_blocks, a.log2_bs,
                            a.scale_log2e, a.ws_m, a.ws_l, a.ws_o, a.key_scale, a.value_scale);
@@ -1020,7 +1030,7 @@ hipError_t launch_decode(const DecodeArgs &a, bool bf16, int head_dim, int group
                            : launch_decode_d<false, 64>(a, group, stream);
 }
 
-hipError_t launch_decode_int8(const DecodeArgs &a, int group, hipStream_t stream) {
+hipError_t launch_decode_q8(const DecodeArgs &a, int group, hipStream_t stream) {
     if (a.num_seqs == 0) return hipSuccess;
     if (a.log2_bs < 4 || a.key_scale == nullptr || a.value_scale == nullptr) return hipErrorInvalidValue;
     switch (group) {

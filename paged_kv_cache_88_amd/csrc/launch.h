@@ -16,9 +16,10 @@ hipError_t launch_gather(void *key_out, void *value_out, const void *key_cache, 
                          const int32_t *block_table_row, int64_t len, int num_kv_heads, int row_bytes,
                          int block_size, int num_blocks, hipStream_t stream);
 
-hipError_t launch_store_int8(bool bf16, int head_dim, const void *key, const void *value, void *key_cache,
-                             void *value_cache, float *key_scale, float *value_scale, const int32_t *slot_mapping,
-                             int64_t num_tokens, int num_kv_heads, int block_size, int num_blocks, hipStream_t stream);
+// 8-bit caches: int8 codes (fp8 false) or OCP float8 E4M3 codes (fp8 true), one fp32 scale per row.
+hipError_t launch_store_q8(bool bf16, bool fp8, int head_dim, const void *key, const void *value, void *key_cache,
+                           void *value_cache, float *key_scale, float *value_scale, const int32_t *slot_mapping,
+                           int64_t num_tokens, int num_kv_heads, int block_size, int num_blocks, hipStream_t stream);
 
 hipError_t launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *pairs, int num_pairs, int64_t block_bytes,
                               int num_blocks, hipStream_t stream);
@@ -48,13 +49,14 @@ struct DecodeArgs {
     float *ws_m;           // [max_items][num_heads]
     float *ws_l;           // [max_items][num_heads]
     float *ws_o;           // [max_items][num_heads][head_dim]
-    const float *key_scale;     // int8 caches only: [num_blocks][num_kv_heads][block_size]
-    const float *value_scale;
+    const float *key_scale = nullptr;     // 8-bit caches only: [num_blocks][num_kv_heads][block_size]
+    const float *value_scale = nullptr;
+    bool fp8_codes = false;               // 8-bit caches: E4M3 codes instead of int8
 };
 
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, int head_dim, int group, hipStream_t stream);
-// int8 caches (codes + per-row scales), bf16 query and output, head_dim 128, block_size >= 16.
-hipError_t launch_decode_int8(const DecodeArgs &a, int group, hipStream_t stream);
+// 8-bit caches (int8 or E4M3 codes + per-row scales), bf16 query and output, head_dim 128, block_size >= 16.
+hipError_t launch_decode_q8(const DecodeArgs &a, int group, hipStream_t stream);
 int decode_max_part_blocks();
 int decode_tile_tokens();
 

@@ -63,19 +63,22 @@ __global__ void __launch_bounds__(256) gather_kernel(u32x4 *__restrict__ key_out
     value_out[row * CHUNKS + chunk] = value_cache[src];
 }
 
-// int8 store ("LLM Infra 101 v0.2: KV Cache", inference-engine list, KV Quantization: K/V kept as int8
-// instead of bf16). Each (token, kv head) row of D elements gets one fp32 scale = max|x| / 127 and codes
-// round_half_even(x / scale) clamped to [-127, 127] (zero rows: scale 0, codes 0), all in fp32 with
-// IEEE division, so the codes are reproducible bit for bit. Codes land in the int8 cache
-// [num_blocks][num_kv_heads][block_size][D] at the slot's row, the scale at the same (block, kv head,
-// offset) of the [num_blocks][num_kv_heads][block_size] scale array.
+// Quantizing store ("LLM Infra 101 v0.2: KV Cache", inference-engine list, KV Quantization: K/V kept in
+// 8 bits instead of bf16). Each (token, kv head) row of D elements gets one fp32 scale and one byte per
+// element, all in fp32 with IEEE division, so codes are reproducible bit for bit:
+//   int8 (F8 false): scale = max|x| / 127, code = round_half_even(x / scale) clamped to [-127, 127];
+//   fp8 (F8 true):   scale = max|x| / 448, code = OCP float8 E4M3 of x / scale, rounded to nearest with
+//                    ties to even by v_cvt_pk_fp8_f32 (|x / scale| <= 448 up to one rounding: never NaN);
+// zero rows get scale 0 and codes 0. Codes land in the cache [num_blocks][num_kv_heads][block_size][D] at
+// the slot's row, the scale at the same (block, kv head, offset) of the [num_blocks][num_kv_heads][block_size]
+// scale array.
 // One row per aligned group of D / 8 lanes, 8 elements per lane; the row max is a DPP butterfly.
-template <bool BF16, int D>
-__global__ void __launch_bounds__(256) store_int8_kernel(const void *__restrict__ key, const void *__restrict__ value,
-                                                         int8_t *__restrict__ key_cache, int8_t *__restrict__ value_cache,
-                                                         float *__restrict__ key_scale, float *__restrict__ value_scale,
-                                                         const int32_t *__restrict__ slot_mapping, int64_t num_rows,
-                                                         int num_kv_heads, int block_size, int num_blocks) {
+template <bool BF16, int D, bool F8>
+__global__ void __launch_bounds__(256) store_q8_kernel(const void *__restrict__ key, const void *__restrict__ value,
+                                                       uint8_t *__restrict__ key_cache, uint8_t *__restrict__ value_cache,
+                                                       float *__restrict__ key_scale, float *__restrict__ value_scale,
+                                                       const int32_t *__restrict__ slot_mapping, int64_t num_rows,
+                                                       int num_kv_heads, int block_size, int num_blocks) {
     constexpr int L = D / 8;               // lanes per row
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t row = gid / L;           // row = token * num_kv_heads + kv head; uniform over the group
@@ -110,39 +113,55 @@ __global__ void __launch_bounds__(256) store_int8_kernel(const void *__restrict_
 #pragma unroll
         for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(x[j]));
         a = group_max<L>(a);
-        const float scale = a / 127.0f;
+        const float scale = a / (F8 ? 448.0f : 127.0f);
         uint32_t packed[2] = {0u, 0u};
+        if constexpr (F8) {
+            float qv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float c = 0.f;
-            if (a > 0.f) c = fminf(fmaxf(__builtin_rintf(x[j] / scale), -127.f), 127.f);
-            packed[j / 4] |= ((uint32_t)(int32_t)c & 0xffu) << (8 * (j % 4));
+            for (int j = 0; j < 8; ++j) qv[j] = a > 0.f ? x[j] / scale : 0.f;
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                int p = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4 * w], qv[4 * w + 1], 0, false);      // bytes 0, 1
+                p = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4 * w + 2], qv[4 * w + 3], p, true);        // bytes 2, 3
+                packed[w] = (uint32_t)p;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float c = 0.f;
+                if (a > 0.f) c = fminf(fmaxf(__builtin_rintf(x[j] / scale), -127.f), 127.f);
+                packed[j / 4] |= ((uint32_t)(int32_t)c & 0xffu) << (8 * (j % 4));
+            }
         }
-        int8_t *dst = (kv ? value_cache : key_cache) + crow * D + 8 * part;
+        uint8_t *dst = (kv ? value_cache : key_cache) + crow * D + 8 * part;
         *(uint2 *)dst = make_uint2(packed[0], packed[1]);
         if (part == 0) (kv ? value_scale : key_scale)[crow] = scale;
     }
 }
 
-hipError_t launch_store_int8(bool bf16, int head_dim, const void *key, const void *value, void *key_cache,
-                             void *value_cache, float *key_scale, float *value_scale, const int32_t *slot_mapping,
-                             int64_t num_tokens, int num_kv_heads, int block_size, int num_blocks, hipStream_t stream) {
+hipError_t launch_store_q8(bool bf16, bool fp8, int head_dim, const void *key, const void *value, void *key_cache,
+                           void *value_cache, float *key_scale, float *value_scale, const int32_t *slot_mapping,
+                           int64_t num_tokens, int num_kv_heads, int block_size, int num_blocks, hipStream_t stream) {
     const int64_t rows = num_tokens * num_kv_heads;
     const int64_t threads = rows * (head_dim / 8);
     if (threads == 0) return hipSuccess;
     dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-    auto kc = (int8_t *)key_cache, vc = (int8_t *)value_cache;
-#define PKV_STORE_I8(B, DD)                                                                                        \
-    hipLaunchKernelGGL((store_int8_kernel<B, DD>), grid, block, 0, stream, key, value, kc, vc, key_scale, value_scale, \
+    auto kc = (uint8_t *)key_cache, vc = (uint8_t *)value_cache;
+#define PKV_STORE_Q8(B, DD, F)                                                                                          \
+    hipLaunchKernelGGL((store_q8_kernel<B, DD, F>), grid, block, 0, stream, key, value, kc, vc, key_scale, value_scale, \
                        slot_mapping, rows, num_kv_heads, block_size, num_blocks)
+#define PKV_STORE_Q8_D(B, F)                  \
+    if (head_dim == 128) PKV_STORE_Q8(B, 128, F); \
+    else PKV_STORE_Q8(B, 64, F)
     if (bf16) {
-        if (head_dim == 128) PKV_STORE_I8(true, 128);
-        else PKV_STORE_I8(true, 64);
+        if (fp8) { PKV_STORE_Q8_D(true, true); }
+        else { PKV_STORE_Q8_D(true, false); }
     } else {
-        if (head_dim == 128) PKV_STORE_I8(false, 128);
-        else PKV_STORE_I8(false, 64);
+        if (fp8) { PKV_STORE_Q8_D(false, true); }
+        else { PKV_STORE_Q8_D(false, false); }
     }
-#undef PKV_STORE_I8
+#undef PKV_STORE_Q8_D
+#undef PKV_STORE_Q8
     return hipGetLastError();
 }
 

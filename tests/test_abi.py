@@ -151,3 +151,21 @@ def test_int8_entry_points_validation(lib):
     assert dec(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 8, 2, 128, 16, 64, 0.1, None, 0, None) == 3
     assert dec(1, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, FAKE, 2, 64, 8, 2, 128, 16, 64, 0.1,
                ctypes.c_void_p(1 << 24), need, None) == 1
+
+
+def test_fp8_entry_points_validation(lib):
+    """fp8 cache calls: the same host-side checks as the int8 ones, refused before any launch."""
+    store = lib.pkv_kv_cache_store_fp8
+    assert store(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 96, 16, 8, None) == 2
+    assert store(1, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 2, 128, 16, 8, None) == 1
+    assert store(1, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 2), FAKE, FAKE, 4, 2, 128, 16, 8, None) == 1
+    assert store(1, None, None, None, None, None, None, None, 0, 2, 128, 16, 8, None) == 0
+    dec = lib.pkv_paged_attention_decode_fp8
+    assert dec(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 10, 8, 2, 128, 16, 64, 0.1, None, 0, None) == 2
+    assert dec(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 10, 8, 2, 64, 16, 64, 0.1, None, 0, None) == 2
+    assert dec(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 10, 8, 2, 128, 8, 64, 0.1, None, 0, None) == 2
+    assert "block_size" in _err(lib)
+    need = lib.pkv_paged_attention_decode_workspace_size(2, 8, 2, 128, 16, 64)
+    assert dec(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 8, 2, 128, 16, 64, 0.1, None, 0, None) == 3
+    assert dec(1, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, FAKE, 2, 64, 8, 2, 128, 16, 64, 0.1,
+               ctypes.c_void_p(1 << 24), need, None) == 1
