@@ -36,6 +36,46 @@ def test_small_ragged(pkv, orc, group, bs):
     assert_close(got, oracle_prefill_case(orc, c), W.BF16, f"prefill g{group} bs{bs}")
 
 
+@pytest.mark.parametrize("bs", [2, 4, 8, 32, 64, 128])
+def test_every_block_size(pkv, orc, bs):
+    """The remaining block sizes: 64 and up gather a 64-key tile from one block, smaller ones row by row."""
+    c = _case(60 + bs, [0, 63, 64, 129, 7], [65, 1, 64, 100, 190], 4, bs)
+    got = run_prefill_case(pkv, c)
+    assert_close(got, oracle_prefill_case(orc, c), W.BF16, f"prefill bs{bs}")
+
+
+@pytest.mark.parametrize("group", [2, 5, 6, 7])
+def test_remaining_groups(pkv, orc, group):
+    """Head groupings whose rows do not fill the workgroup's 128 evenly."""
+    c = _case(70 + group, [0, 40, 300], [97, 33, 150], group, 16)
+    got = run_prefill_case(pkv, c)
+    assert_close(got, oracle_prefill_case(orc, c), W.BF16, f"prefill g{group}")
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_block_table_past_64_blocks(pkv, orc, bs):
+    """Cached prefixes spanning more than 64 blocks (block ids past the first 64 come from the table in
+    memory, not from the lane-held slice): rows near the chunk's end and a sample."""
+    c = _case(80 + bs, [64 * bs + 77, 5], [70, 40], 4, bs)
+    got = run_prefill_case(pkv, c)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(81)
+    rows = np.array(sorted(set(range(c.total_q - 8, c.total_q)) | set(rng.choice(c.total_q, 24, replace=False).tolist())),
+                    np.int32)
+    assert_close(got[rows], oracle_prefill_case(orc, c, rows=rows), W.BF16, f"long table bs{bs}")
+
+
+@pytest.mark.parametrize("n", [64, 65, 130])
+def test_many_sequences(pkv, orc, n):
+    """Batches at and past the size the kernel ranks longest first (64 sequences): every row checked."""
+    rng = np.random.default_rng(90 + n)
+    prefix = rng.integers(0, 200, n).tolist()
+    chunk = rng.integers(1, 80, n).tolist()
+    c = _case(90 + n, prefix, chunk, 4, 16)
+    got = run_prefill_case(pkv, c)
+    assert_close(got, oracle_prefill_case(orc, c), W.BF16, f"{n} sequences")
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_causal_and_full(pkv, orc, causal):
     c = _case(77, [0, 100, 513], [129, 64, 7], 4, 16, causal=causal)
