@@ -131,41 +131,58 @@ def measured_traffic(workload: str):
     return doc["decode_call_traffic_bytes"] if h.hexdigest() == doc["kernel_sources_sha256"] else None
 
 
-def cpu_baseline(c, target_s=12.0):
-    """Time the oracle (float64, all host cores) on a bounded sample of the same workload: the decode of
-    the whole batch, repeated until about target_s seconds of CPU work (fewer sequences if one pass is
-    already longer)."""
+def cpu_baseline(c, target_s=12.0, single_s=3.0):
+    """Time the oracle (float64) on bounded samples of the same workload: on all host cores, the decode of
+    the whole batch repeated until about target_s seconds of CPU work (fewer sequences if one pass is
+    already longer); and on one core, a sample of about single_s seconds."""
     import oracle
 
     orc = oracle.default()
+    cores = int(orc.max_threads())
     kc, vc = c.pool.dense()
     orc.store(c.dtype, c.key, c.value, kc, vc, c.slot_mapping)
     order = np.random.default_rng(0).permutation(c.num_seqs)
-    probe = np.sort(order[:8]).astype(np.int32)
-    t0 = time.perf_counter()
-    orc.decode(c.dtype, c.query, kc, vc, c.block_tables, c.context_lens, c.scale, seqs=probe)
-    per_token = (time.perf_counter() - t0) / max(1, int(c.context_lens[probe].sum()))
-    total_tokens = int(c.context_lens.sum())
-    if per_token * total_tokens >= target_s:
-        cum = np.cumsum(c.context_lens[order])
-        k = max(8, min(c.num_seqs, int(np.searchsorted(cum, target_s / per_token)) + 1))
-        seqs, reps = np.sort(order[:k]).astype(np.int32), 1
-    else:
-        seqs, reps = None, max(1, int(round(target_s / max(per_token * total_tokens, 1e-9))))
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        orc.decode(c.dtype, c.query, kc, vc, c.block_tables, c.context_lens, c.scale, seqs=seqs)
-    dt = time.perf_counter() - t0
-    sel = np.arange(c.num_seqs) if seqs is None else seqs
     e = 2 if c.dtype == "bf16" else 4
-    lens = c.context_lens[sel].astype(np.int64)
-    sample_bytes = reps * int(2 * lens.sum() * c.num_kv_heads * c.head_dim * e + 2 * len(sel) * c.num_heads
-                              * c.head_dim * e + 4 * (-(-lens // c.block_size)).sum() + 4 * len(sel))
-    return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(orc.max_threads()),
-            "kind": "oracle",
-            "sample": f"decode of {len(sel)} of {c.num_seqs} sequences ({int(lens.sum())} context tokens) x {reps} "
-                      f"passes, float64, {dt:.2f} s",
-            "seconds": round(dt, 3), "decode_tokens_per_s": round(reps * len(sel) / dt, 3)}
+
+    def sample_bytes(sel, reps):
+        lens = c.context_lens[sel].astype(np.int64)
+        return reps * int(2 * lens.sum() * c.num_kv_heads * c.head_dim * e + 2 * len(sel) * c.num_heads * c.head_dim * e
+                          + 4 * (-(-lens // c.block_size)).sum() + 4 * len(sel))
+
+    def plan(threads, budget_s):
+        probe = np.sort(order[:8]).astype(np.int32)
+        t0 = time.perf_counter()
+        orc.decode(c.dtype, c.query, kc, vc, c.block_tables, c.context_lens, c.scale, seqs=probe, nthreads=threads)
+        per_token = (time.perf_counter() - t0) / max(1, int(c.context_lens[probe].sum()))
+        if per_token * int(c.context_lens.sum()) >= budget_s:
+            cum = np.cumsum(c.context_lens[order])
+            k = max(8, min(c.num_seqs, int(np.searchsorted(cum, budget_s / per_token)) + 1))
+            return np.sort(order[:k]).astype(np.int32), 1
+        return None, max(1, int(round(budget_s / max(per_token * int(c.context_lens.sum()), 1e-9))))
+
+    def run(threads, seqs, reps):
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            orc.decode(c.dtype, c.query, kc, vc, c.block_tables, c.context_lens, c.scale, seqs=seqs, nthreads=threads)
+        return time.perf_counter() - t0
+
+    seqs, reps = plan(cores, target_s)
+    dt = run(cores, seqs, reps)
+    sel = np.arange(c.num_seqs) if seqs is None else seqs
+    nbytes = sample_bytes(sel, reps)
+    seqs1, reps1 = plan(1, single_s)
+    dt1 = run(1, seqs1, reps1)
+    sel1 = np.arange(c.num_seqs) if seqs1 is None else seqs1
+    nbytes1 = sample_bytes(sel1, reps1)
+    orc.decode(c.dtype, c.query, kc, vc, c.block_tables, c.context_lens, c.scale, seqs=np.sort(order[:1]).astype(np.int32),
+               nthreads=cores)                          # leave the oracle on all cores
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"decode of {len(sel)} of {c.num_seqs} sequences ({int(c.context_lens[sel].sum())} context tokens) "
+                      f"x {reps} passes, float64, {dt:.2f} s",
+            "seconds": round(dt, 3), "decode_tokens_per_s": round(reps * len(sel) / dt, 3),
+            "single_core": {"value": round(nbytes1 / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                            "sample": f"decode of {len(sel1)} sequences ({int(c.context_lens[sel1].sum())} context "
+                                      f"tokens) x {reps1} passes, float64, {dt1:.2f} s"}}
 
 
 def prefill_flops(c) -> int:
@@ -285,11 +302,14 @@ def main():
     ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     n_ev = args.steps
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]     # store start
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]     # store end = decode start
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]     # decode end
 
     def step(k, timed=False):
         kc, vc = pools[k % copies]
+        if timed:
+            evs[k].record(stream)
         pkv.kv_cache_store(kn, vn, kc, vc, sm, stream=stream)
         if timed:
             ev0[k].record(stream)
@@ -309,7 +329,12 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_ms = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)])
+    store_ms = np.array([a.elapsed_time(b) for a, b in zip(evs, ev0)])
     dec_avg_ms = float(dec_ms.mean())
+
+    def dist(x):
+        return {"mean": round(float(x.mean()), 5), "median": round(float(np.median(x)), 5),
+                "p10": round(float(np.percentile(x, 10)), 5), "p90": round(float(np.percentile(x, 90)), 5)}
     achieved = decode_bytes(c) / (dec_avg_ms * 1e-3) / 1e9
     finite = bool(torch.isfinite(out.float()).all().item())
 
@@ -334,13 +359,16 @@ def main():
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(c.num_seqs / (ms_per_step * 1e-3), 1),
         "step_bytes": step_bytes,
-        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode call (decode_kernel + decode_reduce_kernel)",
+        "timing_ms": {"decode_call": dist(dec_ms), "store": dist(store_ms), "events": "HIP events on the launch stream"},
+        "roofline": {"bound": "hbm",
+                     "kernel": "paged_attention_decode call (decode_plan_kernel + decode_mfma_kernel + decode_reduce_kernel)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(c.name),
                      "avg_launch_ms": round(dec_avg_ms, 5), "algorithmic_bytes": decode_bytes(c)},
         "outputs_finite": finite,
         "gpu": torch.cuda.get_device_name(0),
         "torch": torch.__version__,
+        "hip": torch.version.hip,
     }
     if c.dtype == "bf16" and c.head_dim == 128 and c.block_size >= 16 and not args.no_int8:
         pools = None
