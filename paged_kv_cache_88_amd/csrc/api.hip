@@ -75,22 +75,23 @@ pkv_status check_heads(int32_t num_heads, int32_t num_kv_heads) {
 // fixes the bounds it works within:
 //   workers: resident one-wave workgroups, 8 per compute unit (2 per SIMD at the decode kernels'
 //     register budget), capped at DECODE_MAX_WORKERS (MI355X: 256 CUs); the plan aims at
-//     DECODE_UNITS_PER_WORKER units per worker, so a longest-first schedule can even out the ends;
+//     DECODE_MIN_STRATA units per worker, so a longest-first schedule can even out the ends;
 //   max part length: its block-table slice must fit the 64 lanes of a wave (64 blocks when parts start on
 //     a block boundary, i.e. block_size <= 32; 63 otherwise), in whole 32-token tiles;
 //   min part length: DECODE_MIN_PART_TILES tiles, so partials never dominate the traffic.
-// The number of parts is at most 2 B + ceil(target_units / Hkv) + ceil(B * ceil(max_context_len / 32) / max_tiles)
+// The number of parts is at most 2 B + ceil(strata workers / Hkv) + ceil(B * ceil(max_context_len / 32) / max_tiles)
 // (each sequence adds at most one part above its share of the target length and one above its share of
-// the slice limit), which sizes the work list and the partial buffers.
-#ifndef PKV_DECODE_UNITS_PER_WORKER
-#define PKV_DECODE_UNITS_PER_WORKER 1
+// the slice limit; when the plan lengthens parts to fit one unit per worker there are at most
+// strata workers / Hkv), which sizes the work list and the partial buffers.
+#ifndef PKV_DECODE_MIN_STRATA
+#define PKV_DECODE_MIN_STRATA 1
 #endif
 #ifndef PKV_DECODE_WAVES_PER_CU
 #define PKV_DECODE_WAVES_PER_CU 8
 #endif
 constexpr int DECODE_WAVES_PER_CU = PKV_DECODE_WAVES_PER_CU;
 constexpr int DECODE_MAX_WORKERS = 256 * DECODE_WAVES_PER_CU;
-constexpr int DECODE_UNITS_PER_WORKER = PKV_DECODE_UNITS_PER_WORKER;
+constexpr int DECODE_MIN_STRATA = PKV_DECODE_MIN_STRATA;
 constexpr int DECODE_MIN_PART_TILES = 4;
 
 int decode_workers() {
@@ -122,7 +123,7 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
     p.max_part_tiles = slice_blocks * block_size / tile;
     const int64_t max_tiles_per_seq = ((int64_t)(max_context_len > 0 ? max_context_len : 0) + tile - 1) / tile;
     p.max_items = 2 * (int64_t)num_seqs +
-                  ((int64_t)DECODE_MAX_WORKERS * DECODE_UNITS_PER_WORKER + num_kv_heads - 1) / num_kv_heads +
+                  ((int64_t)DECODE_MAX_WORKERS * DECODE_MIN_STRATA + num_kv_heads - 1) / num_kv_heads +
                   ((int64_t)num_seqs * max_tiles_per_seq + p.max_part_tiles - 1) / p.max_part_tiles;
     // [ctrl: 256 B][work list][per-sequence info][partials m, l, o]
     const size_t n = (size_t)p.max_items * num_heads;
@@ -247,7 +248,7 @@ pkv_status decode_args(pkv::DecodeArgs &a, pkv_dtype dtype, void *out, const voi
     a.num_blocks = num_blocks;
     a.log2_bs = log2_exact(block_size);
     a.workers = decode_workers();
-    a.target_units = a.workers * DECODE_UNITS_PER_WORKER;
+    a.min_strata = DECODE_MIN_STRATA;
     a.max_part_tiles = plan.max_part_tiles;
     a.min_part_tiles = DECODE_MIN_PART_TILES;
     a.max_items = plan.max_items;

@@ -93,31 +93,41 @@ __device__ int plan_exclusive_scan(int v, int *s_wave, int *total) {
     return before + x - v;
 }
 
-// Work list. Sequence i (L_i tokens, context_lens clamped to [0, max_context_len]) is cut into n_i
-// parts of len_i tokens, the last part taking the rest, where, in tiles of 32 tokens,
-//   target = max(min_tiles, ceil(num_kv_heads * sum_i ceil(L_i / 32) / target_units)),
-//   n_i    = max(1, round(tiles_i / target), ceil(tiles_i / max_tiles)),  len_i = 32 * ceil(tiles_i / n_i),
-// so the batch is about target_units units of equal size and no part spans more blocks than a lane
-// register holds. items[k] = {seq, first token, tokens, partial slot (-1 when the sequence is one
-// part)}, longest first (64-bucket counting sort; order inside a bucket is arbitrary and every unit
-// writes its own output, so results do not depend on it). seq_info[i] = {first partial slot, n_i,
-// len_i, L_i}; ctrl[0] = number of parts. Sequences with L_i = 0 get zero outputs here. One workgroup; thread t owns sequences t + k * PLAN_THREADS,
-// and keeps the first PLAN_REG of them in registers (larger batches re-read seq_info).
+// Work list. Sequence i (L_i tokens, context_lens clamped to [0, max_context_len], t_i = ceil(L_i / 32)
+// tiles of 32 tokens) is cut into n_i parts of len_i = 32 ceil(t_i / n_i) tokens, the last part taking the
+// rest, with
+//   n_i = max(1, round(t_i / g), ceil(t_i / max_tiles))      (then recounted as ceil(t_i / len_i) tiles)
+// so parts are about g tiles and no part's block-table slice outgrows a lane register. With cap =
+// min_strata W units (W = workers, unit = part x kv head, H = Hkv, T = sum t_i),
+//   g = max(min_tiles, ceil(H T / cap)),
+// which cuts the batch into about cap units of equal size. When every sequence fits one unit per worker
+// (U_min = H sum_i ceil(t_i / max_tiles) <= cap) but rounding leaves U > cap units, g grows (to at least
+// ceil(g U / cap)) and the cut is redone until U <= cap: the few units past a stratum would otherwise run
+// after all the others, each a whole part long. (U_min is summed only for such a batch, and only when the
+// batch has at most cap / H sequences, which any batch that fits has.)
+// items[k] = {seq, first token, tokens, partial slot (-1 when the sequence is one part)}, longest first
+// (64-bucket counting sort; order inside a bucket is arbitrary and every unit writes its own output, so
+// results do not depend on it). seq_info[i] = {first partial slot, n_i, len_i, L_i}; ctrl[0] = number of
+// parts. Sequences with L_i = 0 get zero outputs here. One workgroup; thread t owns sequences
+// t + k * PLAN_THREADS, and keeps the first PLAN_REG of them in registers (larger batches re-read
+// seq_info).
 constexpr int PLAN_REG = 4;
 
 __global__ void __launch_bounds__(PLAN_THREADS)
 decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int max_context_len, int num_kv_heads,
-                   int target_units, int max_tiles, int min_tiles, int4 *__restrict__ items, int4 *__restrict__ seq_info,
+                   int workers, int min_strata, int max_tiles, int min_tiles,
+                   int4 *__restrict__ items, int4 *__restrict__ seq_info,
                    int *__restrict__ ctrl, void *__restrict__ out, int out_row_elems, int elem_bytes) {
     __shared__ int s_wave[PLAN_WAVES];
     __shared__ int hist[PLAN_BUCKETS];
     __shared__ int offs[PLAN_BUCKETS];
-    __shared__ int s_tiles, s_maxlen;
+    __shared__ int s_tiles, s_maxlen, s_umin;
     const int tid = threadIdx.x;
     if (tid < PLAN_BUCKETS) hist[tid] = 0;
     if (tid == 0) {
         s_tiles = 0;
         s_maxlen = 1;
+        s_umin = -1;
     }
     auto clen = [&](int i) { return max(0, min(context_lens[i], max_context_len)); };
     auto wave_sum = [](int v) {
@@ -142,51 +152,77 @@ decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int m
     for (int i = tid + PLAN_REG * PLAN_THREADS; i < num_seqs; i += PLAN_THREADS)
         t += (clen(i) + DECODE_TILE - 1) / DECODE_TILE;
     t = wave_sum(t);
-    __syncthreads();                                  // s_tiles, hist initialised
+    __syncthreads();                                  // s_tiles, s_umin, hist initialised
     if (wave_lead) atomicAdd(&s_tiles, t);
     __syncthreads();
-    const int target = max(min_tiles, (int)(((int64_t)s_tiles * num_kv_heads + target_units - 1) / target_units));
+    const int64_t H = num_kv_heads, cap = (int64_t)workers * min_strata;
+    const int64_t glo = (H * s_tiles + cap - 1) / cap;
+    int target = (int)(glo > min_tiles ? (glo < max_tiles ? glo : max_tiles) : min_tiles);
+    // U_min, computed only when a cut overshoots cap and the batch could fit (num_seqs H <= cap)
+    auto fits = [&]() {
+        if (s_umin < 0) {                             // uniform: s_umin is read after a barrier
+            int um = 0;
+#pragma unroll
+            for (int k = 0; k < PLAN_REG; ++k) um += ((lreg[k] + DECODE_TILE - 1) / DECODE_TILE + max_tiles - 1) / max_tiles;
+            for (int i = tid + PLAN_REG * PLAN_THREADS; i < num_seqs; i += PLAN_THREADS)
+                um += ((clen(i) + DECODE_TILE - 1) / DECODE_TILE + max_tiles - 1) / max_tiles;
+            um = wave_sum(um);
+            __syncthreads();
+            if (tid == 0) s_umin = 0;
+            __syncthreads();
+            if (wave_lead) atomicAdd(&s_umin, um);
+            __syncthreads();
+        }
+        return H * s_umin <= cap;
+    };
 
     // parts per sequence and their partial slots (exclusive scan, PLAN_THREADS sequences at a time)
     int4 sreg[PLAN_REG];
-    int carry = 0, my_max = 1;
-    for (int k = 0, base = 0; base < num_seqs; ++k, base += PLAN_THREADS) {
-        const int i = base + tid;
-        int L = 0, n = 0, len = 0;
-        if (i < num_seqs) {
-            if (k < PLAN_REG) {
-                L = lreg[0];
+    int carry, my_max;
+    for (;;) {                                        // uniform over the workgroup
+        carry = 0;
+        my_max = 1;
+        for (int k = 0, base = 0; base < num_seqs; ++k, base += PLAN_THREADS) {
+            const int i = base + tid;
+            int L = 0, n = 0, len = 0;
+            if (i < num_seqs) {
+                if (k < PLAN_REG) {
+                    L = lreg[0];
 #pragma unroll
-                for (int r = 1; r < PLAN_REG; ++r)
-                    if (r == k) L = lreg[r];
-            } else {
-                L = clen(i);
+                    for (int r = 1; r < PLAN_REG; ++r)
+                        if (r == k) L = lreg[r];
+                } else {
+                    L = clen(i);
+                }
+                const int tiles = (L + DECODE_TILE - 1) / DECODE_TILE;
+                if (tiles > 0) {
+                    n = max(max(1, (tiles + target / 2) / target), (tiles + max_tiles - 1) / max_tiles);
+                    const int lt = (tiles + n - 1) / n;
+                    n = (tiles + lt - 1) / lt;
+                    len = lt * DECODE_TILE;
+                }
             }
-            const int tiles = (L + DECODE_TILE - 1) / DECODE_TILE;
-            if (tiles > 0) {
-                n = max(max(1, (tiles + target / 2) / target), (tiles + max_tiles - 1) / max_tiles);
-                const int lt = (tiles + n - 1) / n;
-                n = (tiles + lt - 1) / lt;
-                len = lt * DECODE_TILE;
-            }
-        }
-        int chunk;
-        const int first = carry + plan_exclusive_scan(n, s_wave, &chunk);
-        const int4 si = make_int4(first, n, len, L);
+            int chunk;
+            const int first = carry + plan_exclusive_scan(n, s_wave, &chunk);
+            const int4 si = make_int4(first, n, len, L);
 #pragma unroll
-        for (int r = 0; r < PLAN_REG; ++r)
-            if (r == k) sreg[r] = si;
-        if (i < num_seqs) {
-            seq_info[i] = si;
-            if (n > 0) {
-                my_max = max(my_max, min(len, L));
-            } else {                                  // empty context: zero outputs for every head
-                const int64_t words = (int64_t)out_row_elems * elem_bytes / 4;
-                uint32_t *o = (uint32_t *)((char *)out + (int64_t)i * out_row_elems * elem_bytes);
-                for (int64_t w = 0; w < words; ++w) o[w] = 0u;
+            for (int r = 0; r < PLAN_REG; ++r)
+                if (r == k) sreg[r] = si;
+            if (i < num_seqs) {
+                seq_info[i] = si;
+                if (n > 0) {
+                    my_max = max(my_max, min(len, L));
+                } else {                              // empty context: zero outputs for every head
+                    const int64_t words = (int64_t)out_row_elems * elem_bytes / 4;
+                    uint32_t *o = (uint32_t *)((char *)out + (int64_t)i * out_row_elems * elem_bytes);
+                    for (int64_t w = 0; w < words; ++w) o[w] = 0u;
+                }
             }
+            carry += chunk;
         }
-        carry += chunk;
+        if (H * carry <= cap || target >= max_tiles || (int64_t)num_seqs * H > cap || !fits()) break;
+        const int64_t grown = ((int64_t)target * H * carry + cap - 1) / cap;
+        target = (int)(grown > target + 1 ? (grown < max_tiles ? grown : max_tiles) : target + 1);
     }
     if (tid == 0) ctrl[0] = carry;
     my_max = wave_max(my_max);
@@ -954,8 +990,8 @@ decode_reduce_kernel(void *__restrict__ out, const int4 *__restrict__ seq_info, 
 template <bool BF16, int D, int G, int NV, int R, int NW, bool MFMA>
 static hipError_t launch_decode_cfg(const DecodeArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, a.context_lens, a.num_seqs,
-                       a.max_context_len, a.num_kv_heads, a.target_units, a.max_part_tiles, a.min_part_tiles, a.items,
-                       a.seq_info, a.ctrl, a.out, a.num_kv_heads * G * D, BF16 ? 2 : 4);
+                       a.max_context_len, a.num_kv_heads, a.workers, a.min_strata, a.max_part_tiles,
+                       a.min_part_tiles, a.items, a.seq_info, a.ctrl, a.out, a.num_kv_heads * G * D, BF16 ? 2 : 4);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t units = (int64_t)a.max_items * a.num_kv_heads;     // upper bound on the unit count

@@ -38,7 +38,8 @@ struct DecodeArgs {
     int64_t num_blocks;    // tokens whose block id lies outside [0, num_blocks) are skipped
     int log2_bs;
     int workers;           // resident one-wave workgroups (persistent grid size)
-    int target_units;      // units the plan aims to cut the batch into
+    int min_strata;        // the plan aims at min_strata * workers units (at most that many when every
+                           // sequence fits one unit per worker)
     int max_part_tiles;    // longest part, in 32-token tiles (its table slice must fit 64 lanes)
     int min_part_tiles;    // shortest part a sequence is split into, in tiles
     int64_t max_items;     // bound on the number of parts (sizes the work list and partials)

@@ -95,6 +95,28 @@ def test_mixed_long_and_short(pkv, orc):
     assert_close(got[seqs], oracle_decode_case(orc, c, seqs=seqs), W.BF16, "mixed")
 
 
+# Batches whose first cut overshoots one unit per resident wave (2048 on MI355X: 256 CUs x 8): the plan
+# lengthens the parts and cuts again (once, twice), or, when the slice limit alone makes more units than
+# waves, keeps the first cut. Each (batch, heads, block) was chosen so that it takes that path at 2048 waves.
+PLAN_RETRY_CASES = [
+    ("recut once", 16, 8, 16, 4000, 0),
+    ("recut twice", 36, 8, 32, 20000, 287),
+    ("overshoot kept", 25, 8, 16, 20000, 10),
+]
+
+
+@pytest.mark.parametrize("name,b,hkv,bs,hi,seed", PLAN_RETRY_CASES, ids=[c[0] for c in PLAN_RETRY_CASES])
+def test_plan_lengthens_parts(pkv, orc, name, b, hkv, bs, hi, seed):
+    lens = np.random.default_rng(seed).integers(1, hi, b).astype(np.int32)
+    nb = int(sum(W.blocks_for_tokens(int(n), bs) for n in lens)) + 2
+    c = W.make_decode_case("recut", 500 + seed, W.BF16, lens, 4 * hkv, hkv, 128, bs, nb)
+    got, _, _ = run_decode_case(pkv, c)
+    seqs = np.array(sorted({int(np.argmax(lens)), int(np.argmin(lens))} |
+                           set(np.random.default_rng(seed + 1).choice(b, 6, replace=False).tolist())), np.int32)
+    assert_close(got[seqs], oracle_decode_case(orc, c, seqs=seqs), W.BF16, name)
+    assert np.isfinite(got).all()
+
+
 def test_maximum_batch(pkv, orc):
     """65535 sequences (the ABI's limit) of 1 to 40 tokens with a few empty ones, fp32, head_dim 64:
     the plan's scan runs over 64 chunks, most of them past the register-resident part."""
