@@ -643,8 +643,13 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
     if ((int)blockIdx.x >= nunits) return;
     // Units are taken from the longest-first list in strata of W: in stratum k wave w takes unit
     // k W + w for even k and k W + W - 1 - w for odd k (snake order, so the long units of one stratum
-    // pair with the short ones of the next); a wave stops at its first index past the list.
-    auto unit_index = [&](int k) { return k * W + ((k & 1) ? W - 1 - (int)blockIdx.x : (int)blockIdx.x); };
+    // pair with the short ones of the next), except that a partial last stratum (k >= 1) runs the other
+    // way: the waves it reaches are then those whose earlier strata summed shortest. A wave stops at its
+    // first index past the list.
+    auto unit_index = [&](int k) {
+        const bool rev = ((k & 1) != 0) != (k > 0 && (k + 1) * W > nunits);
+        return k * W + (rev ? W - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    };
 
     struct Unit {
         int seq, start, ntok, pslot, kvh, first_blk, ntiles;
