@@ -73,9 +73,10 @@ pkv_status check_heads(int32_t num_heads, int32_t num_kv_heads) {
 
 // Decode work sizing. The plan kernel cuts sequences into parts on the device (see decode.hip); the host
 // fixes the bounds it works within:
-//   workers: resident one-wave workgroups, 8 per compute unit (2 per SIMD at the decode kernels'
-//     register budget), capped at DECODE_MAX_WORKERS (MI355X: 256 CUs); the plan aims at
-//     DECODE_MIN_STRATA units per worker, so a longest-first schedule can even out the ends;
+//   workers: resident waves, 8 per compute unit (2 per SIMD at the decode kernels' register budget),
+//     capped at DECODE_MAX_WORKERS (MI355X: 256 CUs); the matrix-core kernel runs 4 of them per compute
+//     unit over bf16 caches and 8 over 8-bit caches. The plan aims at DECODE_MIN_STRATA units per
+//     worker, so a longest-first schedule can even out the ends;
 //   max part length: its block-table slice must fit the 64 lanes of a wave (64 blocks when parts start on
 //     a block boundary, i.e. block_size <= 32; 63 otherwise), in whole 32-token tiles;
 //   min part length: DECODE_MIN_PART_TILES tiles, so partials never dominate the traffic.
@@ -248,6 +249,7 @@ pkv_status decode_args(pkv::DecodeArgs &a, pkv_dtype dtype, void *out, const voi
     a.num_blocks = num_blocks;
     a.log2_bs = log2_exact(block_size);
     a.workers = decode_workers();
+    a.compute_units = a.workers / DECODE_WAVES_PER_CU;
     a.min_strata = DECODE_MIN_STRATA;
     a.max_part_tiles = plan.max_part_tiles;
     a.min_part_tiles = DECODE_MIN_PART_TILES;

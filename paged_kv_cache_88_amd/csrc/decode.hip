@@ -623,8 +623,18 @@ __device__ __forceinline__ uint32_t code_pair_to_bf16x2(uint32_t w) {
     else return i8pair_to_bf16x2(w, K);
 }
 
-template <int G, bool Q8, bool F8>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Waves of one matrix-core decode workgroup (one workgroup per compute unit): one per SIMD over bf16
+// caches; two per SIMD over 8-bit caches, whose tiles carry half the bytes, so a wave alone keeps too
+// few of them in flight.
+constexpr int DECODE_CU_WAVES_BF16 = 4;
+constexpr int DECODE_CU_WAVES_Q8 = 8;
+#ifndef PKV_DECODE_CLAIM_LEAD
+#define PKV_DECODE_CLAIM_LEAD 3
+#endif
+constexpr int DECODE_CLAIM_LEAD = PKV_DECODE_CLAIM_LEAD;  // tiles left in a unit when the next is claimed
+
+template <int G, bool Q8, bool F8, int NWV = Q8 ? DECODE_CU_WAVES_Q8 : DECODE_CU_WAVES_BF16>
+__global__ void __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const char *__restrict__ key_cache,
                    const char *__restrict__ value_cache, const int32_t *__restrict__ block_tables, int bt_stride,
                    const int4 *__restrict__ items, const int *__restrict__ ctrl, int num_kv_heads,
@@ -635,21 +645,35 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
     constexpr int D = 128, CH = D / 8;        // 16-byte chunks of a bf16 row
     constexpr int RB = Q8 ? D : 2 * D;        // bytes per cache row
     constexpr int TILE = 32;
-    const int lane = threadIdx.x, n = lane & 15, b = lane >> 4;
+    const int lane = threadIdx.x & 63, n = lane & 15, b = lane >> 4;
     const int num_heads = num_kv_heads * G;
     const int bs_mask = (1 << log2_bs) - 1;
     const int nunits = ctrl[0] * num_kv_heads;
-    const int W = gridDim.x;
-    if ((int)blockIdx.x >= nunits) return;
-    // Units are taken from the longest-first list in strata of W: in stratum k wave w takes unit
-    // k W + w for even k and k W + W - 1 - w for odd k (snake order, so the long units of one stratum
-    // pair with the short ones of the next), except that a partial last stratum (k >= 1) runs the other
-    // way: the waves it reaches are then those whose earlier strata summed shortest. A wave stops at its
-    // first index past the list.
+    // Units are dealt to the C workgroups (one per compute unit) from the longest-first list in strata
+    // of C: in stratum k workgroup c takes unit k C + c for even k and k C + C - 1 - c for odd k (snake
+    // order, so the long units of one stratum pair with the short ones of the next), except that a
+    // partial last stratum (k >= 1) runs the other way. Inside the workgroup the waves share its strata
+    // through an LDS counter: wave v starts with stratum v and claims each later one shortly before it
+    // needs it, so waves that run faster take more of the list and every wave of the compute unit runs
+    // until the list is done. (Waves do not run at equal rates: of two waves sharing a SIMD the older
+    // one wins arbitration and streams up to twice as fast.) A wave stops at its first stratum whose
+    // unit lies past the list.
+    const int C = gridDim.x, cu = blockIdx.x;
     auto unit_index = [&](int k) {
-        const bool rev = ((k & 1) != 0) != (k > 0 && (k + 1) * W > nunits);
-        return k * W + (rev ? W - 1 - (int)blockIdx.x : (int)blockIdx.x);
+        const bool rev = ((k & 1) != 0) != (k > 0 && (k + 1) * C > nunits);
+        return k * C + (rev ? C - 1 - cu : cu);
     };
+    __shared__ int s_next_stratum;
+    if (threadIdx.x == 0) s_next_stratum = NWV;
+    __syncthreads();
+    auto claim = [&]() {
+        int k = 0;
+        if (lane == 0) k = atomicAdd(&s_next_stratum, 1);
+        return __builtin_amdgcn_readfirstlane(k);
+    };
+    const int wave_id = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform
+    const int first = unit_index(wave_id);
+    if (first >= nunits) return;
 
     struct Unit {
         int seq, start, ntok, pslot, kvh, first_blk, ntiles;
@@ -673,14 +697,14 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
         if (lane < span && x.first_blk + lane < bt_stride) v = block_tables[(int64_t)x.seq * bt_stride + x.first_blk + lane];
         return v;
     };
-    u32x4 qt[4];
-    auto load_q = [&](const Unit &x) {
+    u32x4 qt[4], qn[4];                         // queries of the current unit; of the next one (prefetched)
+    auto load_q = [&](const Unit &x, u32x4 (&dst)[4]) {
         const u32x4 *qv = (const u32x4 *)query;
         const int64_t row = ((int64_t)x.seq * num_heads + x.kvh * G + (n < G ? n : 0)) * CH;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int chunk = Q8 ? (c < 2 ? 2 * b + c : 8 + 2 * b + (c - 2)) : 4 * c + b;
-            qt[c] = n < G ? qv[row + chunk] : u32x4{0, 0, 0, 0};
+            dst[c] = n < G ? qv[row + chunk] : u32x4{0, 0, 0, 0};
         }
     };
 
@@ -875,27 +899,39 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
         for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
 
-    Unit cur = load_unit(blockIdx.x);
+    Unit cur = load_unit(first);
     int cur_blk = load_slice(cur);
-    load_q(cur);
-    int k = 1;                                  // stratum of `nxt`
+    load_q(cur, qt);
+    // The next unit is claimed when the current one has DECODE_CLAIM_LEAD tiles left (at once for shorter
+    // units): late enough that waves which run faster claim more of the workgroup's list, early enough
+    // that its work item, then its block-table slice and queries, then its first tile arrive behind the
+    // current unit's last tiles.
     Unit nxt = cur;
-    bool has_next = unit_index(k) < nunits;
-    if (has_next) nxt = load_unit(unit_index(k));
-    int nxt_blk = -1;
-    bool nxt_ready = false;
+    bool claimed = false, has_next = false, nxt_ready = false;
+    int nxt_blk = -1, claim_ct = 0;
     int ct = 0;                                 // tile of `cur` being computed
+    auto claim_next = [&]() {
+        const int nu = unit_index(claim());
+        has_next = nu < nunits;
+        if (has_next) nxt = load_unit(nu);
+        claimed = true;
+        claim_ct = ct;
+    };
+    auto prepare_next = [&]() {                 // block-table slice and queries of the claimed unit
+        nxt_blk = load_slice(nxt);
+        load_q(nxt, qn);
+        nxt_ready = true;
+    };
+    if (cur.ntiles <= DECODE_CLAIM_LEAD) claim_next();
 
     // one pipeline step: load the tile after `ct` into B (the next unit's first tile when `ct` is the
     // last), compute tile `ct` from A, then advance; false once the wave's last unit is written
     // (one issue site: after the wave's last tile it reloads that tile, which nothing reads)
     auto step = [&](Tile &A, Tile &B) -> bool {
         const bool last = ct + 1 >= cur.ntiles;
+        if (last && !claimed) claim_next();
         const bool go_next = last && has_next;
-        if (go_next && !nxt_ready) {
-            nxt_blk = load_slice(nxt);
-            nxt_ready = true;
-        }
+        if (go_next && !nxt_ready) prepare_next();
         issue(go_next ? nxt : cur, go_next ? nxt_blk : cur_blk, go_next ? 0 : (last ? ct : ct + 1), B);
         compute(cur, ct, A);
         if (!last) {
@@ -906,15 +942,15 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
             cur = nxt;
             cur_blk = nxt_blk;
             ct = 0;
-            load_q(cur);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) qt[c] = qn[c];
+            claimed = false;
             nxt_ready = false;
-            ++k;
-            has_next = unit_index(k) < nunits;
-            if (has_next) nxt = load_unit(unit_index(k));
         }
-        if (has_next && !nxt_ready && ct > 0) {   // the next unit's item has had a step to arrive
-            nxt_blk = load_slice(nxt);
-            nxt_ready = true;
+        if (!claimed) {
+            if (cur.ntiles - ct <= DECODE_CLAIM_LEAD) claim_next();
+        } else if (has_next && !nxt_ready && ct > claim_ct) {
+            prepare_next();                     // the claimed unit's item has had a step to arrive
         }
         return true;
     };
@@ -994,20 +1030,25 @@ decode_reduce_kernel(void *__restrict__ out, const int4 *__restrict__ seq_info, 
 
 template <bool BF16, int D, int G, int NV, int R, int NW, bool MFMA>
 static hipError_t launch_decode_cfg(const DecodeArgs &a, hipStream_t stream) {
+    // resident waves the plan sizes parts for: the matrix-core kernel runs NWV waves per compute unit
+    const bool q8 = a.key_scale != nullptr;
+    const int nwv = q8 ? DECODE_CU_WAVES_Q8 : DECODE_CU_WAVES_BF16;
+    const int workers = MFMA ? a.compute_units * nwv : a.workers;
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, a.context_lens, a.num_seqs,
-                       a.max_context_len, a.num_kv_heads, a.workers, a.min_strata, a.max_part_tiles,
+                       a.max_context_len, a.num_kv_heads, workers, a.min_strata, a.max_part_tiles,
                        a.min_part_tiles, a.items, a.seq_info, a.ctrl, a.out, a.num_kv_heads * G * D, BF16 ? 2 : 4);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t units = (int64_t)a.max_items * a.num_kv_heads;     // upper bound on the unit count
     if constexpr (MFMA) {
         static_assert(BF16 && D == 128, "matrix-core decode: bf16, head_dim 128");
-        const int64_t grid = units < a.workers ? units : a.workers;
-        const bool q8 = a.key_scale != nullptr;
+        // one workgroup of nwv waves per compute unit
+        const int64_t need = (units + nwv - 1) / nwv;
+        const int64_t grid = need < a.compute_units ? need : a.compute_units;
         auto kernel = !q8 ? decode_mfma_kernel<G, false, false>
                           : a.fp8_codes ? decode_mfma_kernel<G, true, true> : decode_mfma_kernel<G, true, false>;
         hipLaunchKernelGGL(kernel, dim3((unsigned)grid),
-                           dim3(64), 0, stream, a.out, a.query, (const char *)a.key_cache, (const char *)a.value_cache,
+                           dim3(64 * nwv), 0, stream, a.out, a.query, (const char *)a.key_cache, (const char *)a.value_cache,
                            a.block_tables, a.bt_stride, a.items, a.ctrl, a.num_kv_heads, a.num_blocks, a.log2_bs,
                            a.scale_log2e, a.ws_m, a.ws_l, a.ws_o, a.key_scale, a.value_scale);
     } else {

@@ -37,7 +37,8 @@ struct DecodeArgs {
     int num_kv_heads;
     int64_t num_blocks;    // tokens whose block id lies outside [0, num_blocks) are skipped
     int log2_bs;
-    int workers;           // resident one-wave workgroups (persistent grid size)
+    int workers;           // resident one-wave workgroups (8 per compute unit)
+    int compute_units;     // compute units (the matrix-core decode runs one workgroup on each)
     int min_strata;        // the plan aims at min_strata * workers units (at most that many when every
                            // sequence fits one unit per worker)
     int max_part_tiles;    // longest part, in 32-token tiles (its table slice must fit 64 lanes)
