@@ -30,6 +30,8 @@
 // pairs of the row, and p.v on the weights of two rows rounded to a bf16 pair (fp32 FMAs for fp32
 // data). The group sum is a DPP butterfly; softmax runs in log2 units (exp2 with scale*log2(e) folded
 // in), and the accumulator is rescaled only when some running max of the wave grows.
+#include <climits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -70,15 +72,30 @@ constexpr int PLAN_WAVES = PLAN_THREADS / 64;
 constexpr int PLAN_BUCKETS = 64;
 constexpr int DECODE_TILE = 32;               // part lengths are multiples of this many tokens
 
+// Inclusive prefix (sum, or max) over the 64 lanes of a wave, with DPP moves instead of LDS permutes:
+// shifts by 1, 2, 4 and 8 lanes inside each 16-lane row, then lane 15 of rows 0 and 2 combined into rows 1
+// and 3, then lane 31 into rows 2 and 3. Lanes a move has no source for take the identity. All 64 lanes
+// must be active.
+template <bool MAX>
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int id = MAX ? INT_MIN : 0;
+    auto op = [](int a, int b) { return MAX ? max(a, b) : a + b; };
+    v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x111, 0xf, 0xf, false));     // row_shr:1
+    v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x112, 0xf, 0xf, false));     // row_shr:2
+    v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x114, 0xf, 0xf, false));     // row_shr:4
+    v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x118, 0xf, 0xf, false));     // row_shr:8
+    v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x142, 0xa, 0xf, false));     // row_bcast:15
+    v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x143, 0xc, 0xf, false));     // row_bcast:31
+    return v;
+}
+// the wave's total (sum or max), wave-uniform
+__device__ __forceinline__ int wave_total_sum(int v) { return __builtin_amdgcn_readlane(wave_incl_scan<false>(v), 63); }
+__device__ __forceinline__ int wave_total_max(int v) { return __builtin_amdgcn_readlane(wave_incl_scan<true>(v), 63); }
+
 // Exclusive prefix sum of v over the plan workgroup; *total gets the sum. Every thread must call it.
 __device__ int plan_exclusive_scan(int v, int *s_wave, int *total) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const int x = wave_incl_scan<false>(v);
     if (lane == 63) s_wave[wave] = x;
     __syncthreads();
     int before = 0, all = 0;
@@ -130,16 +147,6 @@ decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int m
         s_umin = -1;
     }
     auto clen = [&](int i) { return max(0, min(context_lens[i], max_context_len)); };
-    auto wave_sum = [](int v) {
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-        return v;
-    };
-    auto wave_max = [](int v) {
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
-        return v;
-    };
     const bool wave_lead = (tid & 63) == 0;
     int lreg[PLAN_REG];
     int t = 0;
@@ -151,7 +158,7 @@ decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int m
     }
     for (int i = tid + PLAN_REG * PLAN_THREADS; i < num_seqs; i += PLAN_THREADS)
         t += (clen(i) + DECODE_TILE - 1) / DECODE_TILE;
-    t = wave_sum(t);
+    t = wave_total_sum(t);
     __syncthreads();                                  // s_tiles, s_umin, hist initialised
     if (wave_lead) atomicAdd(&s_tiles, t);
     __syncthreads();
@@ -166,7 +173,7 @@ decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int m
             for (int k = 0; k < PLAN_REG; ++k) um += ((lreg[k] + DECODE_TILE - 1) / DECODE_TILE + max_tiles - 1) / max_tiles;
             for (int i = tid + PLAN_REG * PLAN_THREADS; i < num_seqs; i += PLAN_THREADS)
                 um += ((clen(i) + DECODE_TILE - 1) / DECODE_TILE + max_tiles - 1) / max_tiles;
-            um = wave_sum(um);
+            um = wave_total_sum(um);
             __syncthreads();
             if (tid == 0) s_umin = 0;
             __syncthreads();
@@ -225,7 +232,7 @@ decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int m
         target = (int)(grown > target + 1 ? (grown < max_tiles ? grown : max_tiles) : target + 1);
     }
     if (tid == 0) ctrl[0] = carry;
-    my_max = wave_max(my_max);
+    my_max = wave_total_max(my_max);
     if (wave_lead) atomicMax(&s_maxlen, my_max);
     __syncthreads();
     const int maxlen = s_maxlen;
@@ -244,13 +251,7 @@ decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int m
     __syncthreads();
     if (tid < 64) {                                   // exclusive scan of the 64 buckets in one wave
         const int h = hist[tid];
-        int v = h;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int u = __shfl_up(v, o);
-            if (tid >= o) v += u;
-        }
-        offs[tid] = v - h;
+        offs[tid] = wave_incl_scan<false>(h) - h;
     }
     __syncthreads();
     auto emit = [&](int i, const int4 &si) {      // n - 1 full parts share a bucket: one reservation
