@@ -235,11 +235,39 @@ def bench_prefill(pkv, torch, dev, iters=20):
     st_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
     pf_ms = float(np.mean([b.elapsed_time(d) for _, b, d in ev]))
     fl = prefill_flops(c)
-    return {"workload": c.name, "total_q": c.total_q, "prefill_ms": round(pf_ms, 5), "store_ms": round(st_ms, 5),
-            "gflop": round(fl / 1e9, 2), "tflops": round(fl / (pf_ms * 1e-3) / 1e12, 2),
-            "mfma_utilization": round(fl / (pf_ms * 1e-3) / MFMA_BF16_PEAK, 4), "peak_tflops": MFMA_BF16_PEAK / 1e12,
-            "store_gbs": round(store_bytes(c) / (st_ms * 1e-3) / 1e9, 1),
-            "outputs_finite": bool(torch.isfinite(out.float()).all().item())}
+    res = {"workload": c.name, "total_q": c.total_q, "prefill_ms": round(pf_ms, 5), "store_ms": round(st_ms, 5),
+           "gflop": round(fl / 1e9, 2), "tflops": round(fl / (pf_ms * 1e-3) / 1e12, 2),
+           "mfma_utilization": round(fl / (pf_ms * 1e-3) / MFMA_BF16_PEAK, 4), "peak_tflops": MFMA_BF16_PEAK / 1e12,
+           "store_gbs": round(store_bytes(c) / (st_ms * 1e-3) / 1e9, 1),
+           "outputs_finite": bool(torch.isfinite(out.float()).all().item())}
+    # the same prefill over 8-bit caches (every cached row and the chunk quantized by the 8-bit store)
+    kr, vr, slots = W.cached_rows(c.pool)
+    for kind in ("int8", "fp8"):
+        code = torch.int8 if kind == "int8" else torch.uint8
+        kq = torch.zeros(shape, dtype=code, device=dev)
+        vq = torch.zeros(shape, dtype=code, device=dev)
+        ks = torch.zeros(shape[:3], dtype=torch.float32, device=dev)
+        vs = torch.zeros(shape[:3], dtype=torch.float32, device=dev)
+        store = pkv.kv_cache_store_int8 if kind == "int8" else pkv.kv_cache_store_fp8
+        prefill = pkv.paged_attention_prefill_int8 if kind == "int8" else pkv.paged_attention_prefill_fp8
+        store(tt(kr), tt(vr), kq, vq, ks, vs, torch.from_numpy(slots).to(dev), stream=stream)
+        store(kn, vn, kq, vq, ks, vs, sm, stream=stream)
+        ev8 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for k in range(iters + 3):
+            e = ev8[k - 3] if k >= 3 else None
+            if e:
+                e[0].record(stream)
+            prefill(out, q, kq, vq, ks, vs, bt, cq, ck, c.max_seqlen_q, c.max_seqlen_k, c.scale, causal=True,
+                    stream=stream)
+            if e:
+                e[1].record(stream)
+        torch.cuda.synchronize()
+        ms8 = float(np.mean([a.elapsed_time(b) for a, b in ev8]))
+        res[f"{kind}_cache"] = {"prefill_ms": round(ms8, 5), "tflops": round(fl / (ms8 * 1e-3) / 1e12, 2),
+                                "mfma_utilization": round(fl / (ms8 * 1e-3) / MFMA_BF16_PEAK, 4),
+                                "outputs_finite": bool(torch.isfinite(out.float()).all().item())}
+        del kq, vq, ks, vs
+    return res
 
 
 def main():

@@ -8,8 +8,10 @@
  *                               cached prefix plus the chunk;
  *   pkv_kv_cache_gather         inverse of the store for one block table (test helper);
  *   pkv_kv_cache_copy_blocks    copy whole blocks (copy-on-write of shared blocks);
- *   pkv_kv_cache_store_int8, pkv_paged_attention_decode_int8: the same over an int8 cache;
- *   pkv_kv_cache_store_fp8, pkv_paged_attention_decode_fp8: the same over an fp8 (E4M3) cache.
+ *   pkv_kv_cache_store_int8, pkv_paged_attention_decode_int8, pkv_paged_attention_prefill_int8:
+ *                               the same over an int8 cache;
+ *   pkv_kv_cache_store_fp8, pkv_paged_attention_decode_fp8, pkv_paged_attention_prefill_fp8:
+ *                               the same over an fp8 (E4M3) cache.
  *
  * Vocabulary (nano-vllm walkthrough, section 2 context: is_prefill, cu_seqlens_q/k, max_seqlen_q/k,
  * slot_mapping, context_lens, block_tables; "推理运行时", section 分页 KV: logical block j of a
@@ -231,6 +233,35 @@ pkv_status pkv_paged_attention_decode_fp8(pkv_dtype dtype, void *out, const void
                                           int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
                                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
                                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_attention_prefill_int8 / paged_attention_prefill_fp8: pkv_paged_attention_prefill over an int8 or
+ * an fp8 (E4M3) cache (layouts and quantization as for the 8-bit decode above): attention over the
+ * dequantized K/V, code * scale (int8) or value(code) * scale (E4M3). The codes become exact bf16 values in
+ * the workgroup's K/V tiles; q.k runs on MFMA with fp32 accumulation and is multiplied by each key row's
+ * K scale; each softmax weight is multiplied by its row's V scale and rounded to bf16 for p.v (the
+ * denominator sums the unscaled weights). The chunk's rows must be stored (kv_cache_store_int8 / _fp8)
+ * before the call. Same arguments, restrictions (bf16 query and out, head_dim 128) and errors as
+ * pkv_paged_attention_prefill, plus key_scale, value_scale: device fp32 [num_blocks][num_kv_heads]
+ * [block_size], 4-byte aligned (null: PKV_EINVAL).
+ * Source: as pkv_paged_attention_prefill; the 8-bit cache as for pkv_paged_attention_decode_int8.
+ */
+pkv_status pkv_paged_attention_prefill_int8(pkv_dtype dtype, void *out, const void *query, const int8_t *key_cache,
+                                            const int8_t *value_cache, const float *key_scale,
+                                            const float *value_scale, const int32_t *block_tables,
+                                            int32_t block_table_stride, const int32_t *cu_seqlens_q,
+                                            const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                                            int32_t max_seqlen_k, int32_t num_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                            int32_t causal, hipStream_t stream);
+pkv_status pkv_paged_attention_prefill_fp8(pkv_dtype dtype, void *out, const void *query, const uint8_t *key_cache,
+                                           const uint8_t *value_cache, const float *key_scale,
+                                           const float *value_scale, const int32_t *block_tables,
+                                           int32_t block_table_stride, const int32_t *cu_seqlens_q,
+                                           const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                                           int32_t max_seqlen_k, int32_t num_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                           int32_t causal, hipStream_t stream);
 
 /* Message of the calling thread's last non-OK status ("" if none). Owned by the library. */
 const char *pkv_last_error(void);

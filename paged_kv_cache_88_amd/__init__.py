@@ -53,6 +53,10 @@ def load_library(path: str = LIB_PATH):
         "pkv_kv_cache_store_fp8": [ctypes.c_int, P, P, P, P, P, P, P, I64, I32, I32, I32, I64, P],
         "pkv_paged_attention_decode_fp8": [ctypes.c_int, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32,
                                            I64, F, P, SZ, P],
+        "pkv_paged_attention_prefill_int8": [ctypes.c_int, P, P, P, P, P, P, P, I32, P, P, I32, I32, I32, I32, I32,
+                                             I32, I32, I64, F, I32, P],
+        "pkv_paged_attention_prefill_fp8": [ctypes.c_int, P, P, P, P, P, P, P, I32, P, P, I32, I32, I32, I32, I32,
+                                            I32, I32, I64, F, I32, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -292,6 +296,47 @@ def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, cu
                                            _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), b, int(max_seqlen_q),
                                            int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), int(bool(causal)),
                                            _stream(stream)))
+
+
+def _prefill_q8(kind, out, query, key_cache, value_cache, key_scale, value_scale, block_tables, cu_seqlens_q,
+                cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal, stream):
+    lib = load_library()
+    _dev(out, query, key_cache, value_cache, key_scale, value_scale, block_tables, cu_seqlens_q, cu_seqlens_k)
+    _i32(block_tables, cu_seqlens_q, cu_seqlens_k)
+    nb, hkv, bs, d = key_cache.shape
+    tq, hq, d2 = query.shape
+    b = cu_seqlens_q.shape[0] - 1
+    if d2 != d or out.shape != query.shape or value_cache.shape != key_cache.shape:
+        raise ValueError("query/out must be [total_q, Hq, D] with the caches' D")
+    if key_scale.shape != (nb, hkv, bs) or value_scale.shape != (nb, hkv, bs):
+        raise ValueError("scales must be [NB, Hkv, bs]")
+    if key_cache.dtype not in _CODE_DTYPES[kind] or value_cache.dtype not in _CODE_DTYPES[kind] \
+            or key_scale.dtype != torch.float32 or value_scale.dtype != torch.float32:
+        raise ValueError(f"{kind} caches and float32 scales expected")
+    if cu_seqlens_k.shape != cu_seqlens_q.shape or b < 0 or block_tables.dim() != 2 or block_tables.shape[0] != b:
+        raise ValueError("cu_seqlens_q/k must be [B+1] and block_tables [B, stride]")
+    fn = lib.pkv_paged_attention_prefill_int8 if kind == "int8" else lib.pkv_paged_attention_prefill_fp8
+    _check(fn(_dtype_code(query), _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(key_scale),
+              _ptr(value_scale), _ptr(block_tables), block_tables.shape[1], _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+              b, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, bs, nb, float(scale), int(bool(causal)),
+              _stream(stream)))
+
+
+def paged_attention_prefill_int8(out, query, key_cache, value_cache, key_scale, value_scale, block_tables,
+                                 cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal=True,
+                                 stream=None):
+    """``paged_attention_prefill`` over an int8 cache (codes [NB, Hkv, bs, D], fp32 scales [NB, Hkv, bs]);
+    bf16 ``out``/``query`` [total_q, Hq, D], D = 128. The chunk must be stored with ``kv_cache_store_int8``."""
+    _prefill_q8("int8", out, query, key_cache, value_cache, key_scale, value_scale, block_tables, cu_seqlens_q,
+                cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal, stream)
+
+
+def paged_attention_prefill_fp8(out, query, key_cache, value_cache, key_scale, value_scale, block_tables,
+                                cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal=True,
+                                stream=None):
+    """``paged_attention_prefill_int8`` over an fp8 (E4M3) cache (code bytes as uint8 or torch.float8_e4m3fn)."""
+    _prefill_q8("fp8", out, query, key_cache, value_cache, key_scale, value_scale, block_tables, cu_seqlens_q,
+                cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal, stream)
 
 
 def kv_cache_copy_blocks(key_cache, value_cache, pairs, stream=None):

@@ -378,13 +378,17 @@ pkv_status pkv_paged_attention_decode_fp8(pkv_dtype dtype, void *out, const void
                      workspace_bytes, stream);
 }
 
-pkv_status pkv_paged_attention_prefill(pkv_dtype dtype, void *out, const void *query, const void *key_cache,
-                                       const void *value_cache, const int32_t *block_tables,
-                                       int32_t block_table_stride, const int32_t *cu_seqlens_q,
-                                       const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
-                                       int32_t max_seqlen_k, int32_t num_heads, int32_t num_kv_heads,
-                                       int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
-                                       int32_t causal, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of a prefill call and its launch arguments (shared by the bf16 and the 8-bit-cache entry points);
+// PKV_OK with nothing to launch when num_seqs or max_seqlen_q is 0.
+pkv_status prefill_args(pkv::PrefillArgs &a, pkv_dtype dtype, void *out, const void *query, const void *key_cache,
+                        const void *value_cache, const int32_t *block_tables, int32_t block_table_stride,
+                        const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t num_seqs,
+                        int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale, int32_t causal) {
     pkv_status st = check_common(dtype, num_kv_heads, head_dim, block_size, num_blocks);
     if (st != PKV_OK) return st;
     st = check_heads(num_heads, num_kv_heads);
@@ -408,7 +412,7 @@ pkv_status pkv_paged_attention_prefill(pkv_dtype dtype, void *out, const void *q
             "out, query and cache pointers must be 16-byte aligned");
     REQUIRE((int64_t)num_seqs * num_kv_heads * ((max_seqlen_q + 15) / 16 + 8) <= ((int64_t)1 << 26), PKV_EINVAL,
             "prefill grid too large");
-    pkv::PrefillArgs a{};
+    a = pkv::PrefillArgs{};
     a.out = out;
     a.query = query;
     a.key_cache = key_cache;
@@ -425,8 +429,76 @@ pkv_status pkv_paged_attention_prefill(pkv_dtype dtype, void *out, const void *q
     a.log2_bs = log2_exact(block_size);
     a.scale_log2e = scale * 1.4426950408889634f;
     a.causal = causal ? 1 : 0;
+    return ok();
+}
+
+pkv_status prefill_q8(bool fp8, const char *what, pkv_dtype dtype, void *out, const void *query,
+                      const void *key_cache, const void *value_cache, const float *key_scale,
+                      const float *value_scale, const int32_t *block_tables, int32_t block_table_stride,
+                      const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t num_seqs,
+                      int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale, int32_t causal,
+                      hipStream_t stream) {
+    pkv::PrefillArgs a{};
+    const pkv_status st = prefill_args(a, dtype, out, query, key_cache, value_cache, block_tables, block_table_stride,
+                                       cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q, max_seqlen_k, num_heads,
+                                       num_kv_heads, head_dim, block_size, num_blocks, scale, causal);
+    if (st != PKV_OK || num_seqs == 0 || max_seqlen_q == 0) return st;
+    REQUIRE(key_scale && value_scale, PKV_EINVAL, "null scale array");
+    REQUIRE(((uintptr_t)key_scale & 3u) == 0 && ((uintptr_t)value_scale & 3u) == 0, PKV_EINVAL,
+            "scale arrays must be 4-byte aligned");
+    a.key_scale = key_scale;
+    a.value_scale = value_scale;
+    a.fp8_codes = fp8;
+    return hip_status(pkv::launch_prefill_q8(a, num_heads / num_kv_heads, stream), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attention_prefill(pkv_dtype dtype, void *out, const void *query, const void *key_cache,
+                                       const void *value_cache, const int32_t *block_tables,
+                                       int32_t block_table_stride, const int32_t *cu_seqlens_q,
+                                       const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                                       int32_t max_seqlen_k, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                       int32_t causal, hipStream_t stream) {
+    pkv::PrefillArgs a{};
+    const pkv_status st = prefill_args(a, dtype, out, query, key_cache, value_cache, block_tables, block_table_stride,
+                                       cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q, max_seqlen_k, num_heads,
+                                       num_kv_heads, head_dim, block_size, num_blocks, scale, causal);
+    if (st != PKV_OK || num_seqs == 0 || max_seqlen_q == 0) return st;
     return hip_status(pkv::launch_prefill(a, true, head_dim, num_heads / num_kv_heads, stream),
                       "paged_attention_prefill launch");
+}
+
+pkv_status pkv_paged_attention_prefill_int8(pkv_dtype dtype, void *out, const void *query, const int8_t *key_cache,
+                                            const int8_t *value_cache, const float *key_scale,
+                                            const float *value_scale, const int32_t *block_tables,
+                                            int32_t block_table_stride, const int32_t *cu_seqlens_q,
+                                            const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                                            int32_t max_seqlen_k, int32_t num_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                            int32_t causal, hipStream_t stream) {
+    return prefill_q8(false, "paged_attention_prefill_int8 launch", dtype, out, query, key_cache, value_cache,
+                      key_scale, value_scale, block_tables, block_table_stride, cu_seqlens_q, cu_seqlens_k, num_seqs,
+                      max_seqlen_q, max_seqlen_k, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                      causal, stream);
+}
+
+pkv_status pkv_paged_attention_prefill_fp8(pkv_dtype dtype, void *out, const void *query, const uint8_t *key_cache,
+                                           const uint8_t *value_cache, const float *key_scale,
+                                           const float *value_scale, const int32_t *block_tables,
+                                           int32_t block_table_stride, const int32_t *cu_seqlens_q,
+                                           const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                                           int32_t max_seqlen_k, int32_t num_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                           int32_t causal, hipStream_t stream) {
+    return prefill_q8(true, "paged_attention_prefill_fp8 launch", dtype, out, query, key_cache, value_cache,
+                      key_scale, value_scale, block_tables, block_table_stride, cu_seqlens_q, cu_seqlens_k, num_seqs,
+                      max_seqlen_q, max_seqlen_k, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                      causal, stream);
 }
 
 }  // extern "C"

@@ -79,8 +79,13 @@ struct PrefillArgs {
     int log2_bs;
     float scale_log2e;
     int causal;
+    const float *key_scale = nullptr;     // 8-bit caches only: [num_blocks][num_kv_heads][block_size]
+    const float *value_scale = nullptr;
+    bool fp8_codes = false;               // 8-bit caches: E4M3 codes instead of int8
 };
 
 hipError_t launch_prefill(const PrefillArgs &a, bool bf16, int head_dim, int group, hipStream_t stream);
+// 8-bit caches (int8 or E4M3 codes + per-row scales), bf16 query and output, head_dim 128.
+hipError_t launch_prefill_q8(const PrefillArgs &a, int group, hipStream_t stream);
 
 }  // namespace pkv

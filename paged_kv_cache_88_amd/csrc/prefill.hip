@@ -71,21 +71,45 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *p) {
 
 // QB: 16-row blocks per wave (rows per wave 16 QB, per workgroup 64 QB). Every K and V^T value read from
 // LDS feeds QB MFMAs, so LDS traffic per MFMA falls as QB grows; QB = 4 takes one wave per SIMD.
-template <int G, int QB>
+//
+// 8-bit caches (Q8): rows hold one-byte codes (int8, or OCP float8 E4M3 when F8) with one fp32 scale per
+// (token, kv head). The gather loads the codes and the tile's 64 key and 64 value scales; codes become exact
+// bf16 values as the tile is stored to LDS, so the rest of the tile's work is the bf16 path's. The K scale
+// multiplies each score (before the mask), and the V scale each weight before it is rounded to bf16; the
+// denominator sums the unscaled weights (so out = sum_t p_t v_t scale_t / sum_t p_t, the attention over the
+// dequantized rows).
+template <bool F8, int K>
+__device__ __forceinline__ uint32_t pf_code_pair_to_bf16x2(uint32_t w) {
+    if constexpr (F8) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, K != 0));
+    else return i8pair_to_bf16x2(w, K);
+}
+// 16 codes -> 16 bf16 values in order (two 16-byte LDS stores)
+template <bool F8>
+__device__ __forceinline__ void pf_codes_to_bf16(const u32x4 c, u32x4 &lo, u32x4 &hi) {
+    lo = u32x4{pf_code_pair_to_bf16x2<F8, 0>(c[0]), pf_code_pair_to_bf16x2<F8, 1>(c[0]),
+               pf_code_pair_to_bf16x2<F8, 0>(c[1]), pf_code_pair_to_bf16x2<F8, 1>(c[1])};
+    hi = u32x4{pf_code_pair_to_bf16x2<F8, 0>(c[2]), pf_code_pair_to_bf16x2<F8, 1>(c[2]),
+               pf_code_pair_to_bf16x2<F8, 0>(c[3]), pf_code_pair_to_bf16x2<F8, 1>(c[3])};
+}
+
+template <int G, int QB, bool Q8 = false, bool F8 = false>
 __global__ void __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(QB <= 2 ? 2 : 1, QB <= 2 ? 2 : 1)))
 prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, const u32x4 *__restrict__ key_cache,
                const u32x4 *__restrict__ value_cache, const int32_t *__restrict__ block_tables, int bt_stride,
                const int32_t *__restrict__ cu_seqlens_q, const int32_t *__restrict__ cu_seqlens_k, int num_seqs,
                int max_seqlen_k, int num_q_tiles, int num_kv_heads, int64_t num_blocks, int log2_bs, float scale_log2e,
-               int causal) {
+               int causal, const float *__restrict__ key_scale = nullptr, const float *__restrict__ value_scale = nullptr) {
     constexpr int WROWS = 16 * QB;            // rows per wave
     constexpr int ROWS = 4 * WROWS;           // rows per workgroup
     constexpr int BQ = ROWS / G;              // query positions per workgroup
     constexpr int VR = BQ * G;                // rows in use (<= ROWS)
-    constexpr int CH = PF_D / 8;              // 16-byte chunks per K/V row
+    constexpr int CH = PF_D / 8;              // 16-byte chunks per bf16 row (query, LDS tiles)
+    constexpr int RCH = Q8 ? PF_D / 16 : CH;  // 16-byte chunks per cache row
+    constexpr int NC = PF_BN * RCH / PF_THREADS;   // cache chunks of a tile per thread (K, and V): 4 or 2
 
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][PF_BN * PF_KPAD];     // double-buffered tiles
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][PF_BN * PF_KPAD];
+    __shared__ __attribute__((aligned(16))) float sS[2][2][Q8 ? PF_BN : 1];         // [buf][K, V][key] scales
 
     // linear id w runs on XCD w % 8: group g = (sequence rank, kv head) lives on XCD g % 8
     const int w = blockIdx.x, xcd = w & (PF_XCDS - 1), j = w / PF_XCDS;
@@ -153,8 +177,10 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
         for (int ks = 0; ks < 4; ++ks) qb_reg[qb][ks] = row_ok[qb] ? query[qrow + lb + 4 * ks] : u32x4{0, 0, 0, 0};
     }
 
-    // gather roles: thread tid moves 16-byte chunks tid + 256 c (c < 4) of the K and of the V tile
-    u32x4 kreg[4], vreg[4];
+    // gather roles: thread tid moves 16-byte cache chunks tid + 256 c (c < NC) of the K and of the V tile;
+    // over 8-bit caches threads 0..63 also move the key scale of key tid, threads 64..127 the value scale
+    u32x4 kreg[NC], vreg[NC];
+    float sreg = 0.f;
     // the first 64 block ids of the sequence, one per lane (uniform tiles read them with readlane)
     const int nblk_seq = (Lk + bs_mask) >> log2_bs;
     const int my_blk = lane < nblk_seq ? bt[lane] : -1;
@@ -168,41 +194,71 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
             const int64_t blk = __builtin_amdgcn_readfirstlane(j < 64 ? __builtin_amdgcn_readlane(my_blk, j) : bt[j]);
             const bool ok = blk >= 0 && blk < num_blocks;
             const int64_t slab = ((ok ? blk : 0) * num_kv_heads + kvh) << log2_bs;       // first row
-            const int range = ok ? (int)((uint32_t)PF_D * 2u << log2_bs) : 0;
+            const int range = ok ? (int)((uint32_t)RCH * 16u << log2_bs) : 0;
             const __amdgpu_buffer_rsrc_t kr =
-                __builtin_amdgcn_make_buffer_rsrc((void *)(key_cache + slab * CH), (short)0, range, PF_BUF_W3);
+                __builtin_amdgcn_make_buffer_rsrc((void *)(key_cache + slab * RCH), (short)0, range, PF_BUF_W3);
             const __amdgpu_buffer_rsrc_t vr =
-                __builtin_amdgcn_make_buffer_rsrc((void *)(value_cache + slab * CH), (short)0, range, PF_BUF_W3);
-            const int soff = (key0 & bs_mask) * PF_D * 2;
+                __builtin_amdgcn_make_buffer_rsrc((void *)(value_cache + slab * RCH), (short)0, range, PF_BUF_W3);
+            const int soff = (key0 & bs_mask) * RCH * 16;
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+            for (int c = 0; c < NC; ++c)
                 kreg[c] = __builtin_amdgcn_raw_buffer_load_b128(kr, (tid + c * PF_THREADS) * 16, soff, 0);
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+            for (int c = 0; c < NC; ++c)
                 vreg[c] = __builtin_amdgcn_raw_buffer_load_b128(vr, (tid + c * PF_THREADS) * 16, soff, 0);
+            if constexpr (Q8) {
+                if (tid < 2 * PF_BN) {
+                    const float *sc = tid < PF_BN ? key_scale : value_scale;
+                    sreg = ok ? sc[slab + (key0 & bs_mask) + (tid & (PF_BN - 1))] : 0.f;
+                }
+            }
             return;
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < NC; ++c) {
             const int idx = tid + c * PF_THREADS;
-            const int gk = key0 + idx / CH, ch = idx % CH;
+            const int gk = key0 + idx / RCH, ch = idx % RCH;
             kreg[c] = vreg[c] = u32x4{0, 0, 0, 0};
             if (gk < kend) {
                 const int64_t blk = bt[gk >> log2_bs];
                 if (blk >= 0 && blk < num_blocks) {
                     const int64_t row = ((blk * num_kv_heads + kvh) << log2_bs) + (gk & bs_mask);
-                    kreg[c] = key_cache[row * CH + ch];
-                    vreg[c] = value_cache[row * CH + ch];
+                    kreg[c] = key_cache[row * RCH + ch];
+                    vreg[c] = value_cache[row * RCH + ch];
                 }
+            }
+        }
+        if constexpr (Q8) {                     // scales of keys past the end or outside the pool: 0
+            sreg = 0.f;
+            const int gk = key0 + (tid & (PF_BN - 1));
+            if (tid < 2 * PF_BN && gk < kend) {
+                const int64_t blk = bt[gk >> log2_bs];
+                if (blk >= 0 && blk < num_blocks)
+                    sreg = (tid < PF_BN ? key_scale : value_scale)[((blk * num_kv_heads + kvh) << log2_bs) + (gk & bs_mask)];
             }
         }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < NC; ++c) {
             const int idx = tid + c * PF_THREADS;
-            *(u32x4 *)&sK[buf][(idx / CH) * PF_KPAD + (idx % CH) * 8] = kreg[c];
-            *(u32x4 *)&sV[buf][(idx / CH) * PF_KPAD + (idx % CH) * 8] = vreg[c];
+            if constexpr (Q8) {                  // 16 codes -> dims 16 ch .. +16 of the row, as bf16
+                u32x4 lo, hi;
+                uint16_t *kp = &sK[buf][(idx / RCH) * PF_KPAD + (idx % RCH) * 16];
+                uint16_t *vp = &sV[buf][(idx / RCH) * PF_KPAD + (idx % RCH) * 16];
+                pf_codes_to_bf16<F8>(kreg[c], lo, hi);
+                *(u32x4 *)kp = lo;
+                *(u32x4 *)(kp + 8) = hi;
+                pf_codes_to_bf16<F8>(vreg[c], lo, hi);
+                *(u32x4 *)vp = lo;
+                *(u32x4 *)(vp + 8) = hi;
+            } else {
+                *(u32x4 *)&sK[buf][(idx / CH) * PF_KPAD + (idx % CH) * 8] = kreg[c];
+                *(u32x4 *)&sV[buf][(idx / CH) * PF_KPAD + (idx % CH) * 8] = vreg[c];
+            }
+        }
+        if constexpr (Q8) {
+            if (tid < 2 * PF_BN) sS[buf][tid / PF_BN][tid & (PF_BN - 1)] = sreg;
         }
     };
 
@@ -241,6 +297,17 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
             }
         }
 
+        // 8-bit caches: each score times its key's scale (keys 16 kb + 4 lb + i), before the mask
+        f32x4 vsc[4];
+        if constexpr (Q8) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const f32x4 ks = *(const f32x4 *)&sS[cur][0][kb * 16 + lb * 4];
+                vsc[kb] = *(const f32x4 *)&sS[cur][1][kb * 16 + lb * 4];
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) s[kb][qb] *= ks;
+            }
+        }
         // mask, online softmax per row, rounded weights packed as the B operand of O^T += V^T P^T
         // (scores stay unscaled until the exponent: scale > 0 keeps the max; m is kept in scaled units)
         if constexpr (MASKED) {                              // some key of this tile is hidden from a row
@@ -291,13 +358,26 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     const int kb = 2 * ks + half;
-                    w[2 * half] = pack_bf16x2(fast_exp2(fmaf(s[kb][qb][0], scale_log2e, nm)),
-                                              fast_exp2(fmaf(s[kb][qb][1], scale_log2e, nm)));
-                    w[2 * half + 1] = pack_bf16x2(fast_exp2(fmaf(s[kb][qb][2], scale_log2e, nm)),
-                                                  fast_exp2(fmaf(s[kb][qb][3], scale_log2e, nm)));
-                }
+                    if constexpr (Q8) {          // weights times the V scales; the sum takes them unscaled
+                        float p[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) rs = dot2_bf16(w[e], 0x3f803f80u, rs);   // sum of the rounded weights
+                        for (int i = 0; i < 4; ++i) {
+                            p[i] = fast_exp2(fmaf(s[kb][qb][i], scale_log2e, nm));
+                            rs += p[i];
+                        }
+                        w[2 * half] = pack_bf16x2(p[0] * vsc[kb][0], p[1] * vsc[kb][1]);
+                        w[2 * half + 1] = pack_bf16x2(p[2] * vsc[kb][2], p[3] * vsc[kb][3]);
+                    } else {
+                        w[2 * half] = pack_bf16x2(fast_exp2(fmaf(s[kb][qb][0], scale_log2e, nm)),
+                                                  fast_exp2(fmaf(s[kb][qb][1], scale_log2e, nm)));
+                        w[2 * half + 1] = pack_bf16x2(fast_exp2(fmaf(s[kb][qb][2], scale_log2e, nm)),
+                                                      fast_exp2(fmaf(s[kb][qb][3], scale_log2e, nm)));
+                    }
+                }
+                if constexpr (!Q8) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rs = dot2_bf16(w[e], 0x3f803f80u, rs);   // sum of the rounded weights
+                }
                 pb[ks][qb] = u32x4{w[0], w[1], w[2], w[3]};
             }
             l[qb] += rs;
@@ -350,18 +430,40 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
 #define PKV_PREFILL_QB 2
 #endif
 
-template <int G>
+template <int G, bool Q8 = false, bool F8 = false>
 static hipError_t launch_prefill_g(const PrefillArgs &a, hipStream_t stream) {
     constexpr int QB = PKV_PREFILL_QB;
     constexpr int BQ = 64 * QB / G;
     const int num_q_tiles = (a.max_seqlen_q + BQ - 1) / BQ;
     const int64_t groups = (int64_t)a.num_seqs * a.num_kv_heads;
     const int64_t wgs = (groups + PF_XCDS - 1) / PF_XCDS * PF_XCDS * num_q_tiles;
-    hipLaunchKernelGGL((prefill_kernel<G, QB>), dim3((unsigned)wgs), dim3(PF_THREADS), 0, stream, (uint16_t *)a.out,
-                       (const u32x4 *)a.query, (const u32x4 *)a.key_cache, (const u32x4 *)a.value_cache, a.block_tables,
-                       a.bt_stride, a.cu_seqlens_q, a.cu_seqlens_k, a.num_seqs, a.max_seqlen_k, num_q_tiles,
-                       a.num_kv_heads, a.num_blocks, a.log2_bs, a.scale_log2e, a.causal);
+    hipLaunchKernelGGL((prefill_kernel<G, QB, Q8, F8>), dim3((unsigned)wgs), dim3(PF_THREADS), 0, stream,
+                       (uint16_t *)a.out, (const u32x4 *)a.query, (const u32x4 *)a.key_cache,
+                       (const u32x4 *)a.value_cache, a.block_tables, a.bt_stride, a.cu_seqlens_q, a.cu_seqlens_k,
+                       a.num_seqs, a.max_seqlen_k, num_q_tiles, a.num_kv_heads, a.num_blocks, a.log2_bs,
+                       a.scale_log2e, a.causal, a.key_scale, a.value_scale);
     return hipGetLastError();
+}
+
+template <bool F8>
+static hipError_t launch_prefill_q8_f(const PrefillArgs &a, int group, hipStream_t stream) {
+    switch (group) {
+        case 1: return launch_prefill_g<1, true, F8>(a, stream);
+        case 2: return launch_prefill_g<2, true, F8>(a, stream);
+        case 3: return launch_prefill_g<3, true, F8>(a, stream);
+        case 4: return launch_prefill_g<4, true, F8>(a, stream);
+        case 5: return launch_prefill_g<5, true, F8>(a, stream);
+        case 6: return launch_prefill_g<6, true, F8>(a, stream);
+        case 7: return launch_prefill_g<7, true, F8>(a, stream);
+        case 8: return launch_prefill_g<8, true, F8>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_prefill_q8(const PrefillArgs &a, int group, hipStream_t stream) {
+    if (a.num_seqs == 0 || a.max_seqlen_q == 0) return hipSuccess;
+    if (!a.key_scale || !a.value_scale) return hipErrorInvalidValue;
+    return a.fp8_codes ? launch_prefill_q8_f<true>(a, group, stream) : launch_prefill_q8_f<false>(a, group, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, bool bf16, int head_dim, int group, hipStream_t stream) {

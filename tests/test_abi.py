@@ -122,6 +122,23 @@ def test_prefill_validation(lib):
     assert call(1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, FAKE, 2, 8, 64, 8, 2, 128, 16, 64, 0.1, 1, None) == 1
 
 
+@pytest.mark.parametrize("name", ["pkv_paged_attention_prefill_int8", "pkv_paged_attention_prefill_fp8"])
+def test_prefill_q8_validation(lib, name):
+    """8-bit-cache prefill: the bf16 prefill's checks, plus the scale arrays, refused before any launch."""
+    call = getattr(lib, name)
+    # (dtype, out, q, kc, vc, ks, vs, bt, stride, cu_q, cu_k, B, max_q, max_k, Hq, Hkv, D, bs, NB, scale, causal, stream)
+    assert call(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 2, 8, 64, 8, 2, 128, 16, 64, 0.1, 1, None) == 2
+    assert call(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 2, 8, 64, 8, 2, 64, 16, 64, 0.1, 1, None) == 2
+    assert call(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 2, 65, 64, 8, 2, 128, 16, 64, 0.1, 1, None) == 1
+    assert call(1, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, FAKE, FAKE, 2, 8, 64, 8, 2, 128, 16, 64, 0.1, 1, None) == 1
+    assert "scale" in _err(lib)
+    assert call(1, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 2), FAKE, 4, FAKE, FAKE, 2, 8, 64, 8, 2,
+                128, 16, 64, 0.1, 1, None) == 1
+    # nothing to do: no sequences, or no query rows
+    assert call(1, None, None, None, None, None, None, None, 4, None, None, 0, 8, 64, 8, 2, 128, 16, 64, 0.1, 1, None) == 0
+    assert call(1, None, None, None, None, None, None, None, 4, None, None, 2, 0, 64, 8, 2, 128, 16, 64, 0.1, 1, None) == 0
+
+
 def test_binding_fails_loudly_without_library(pkv, tmp_path):
     saved = pkv._lib
     try:
