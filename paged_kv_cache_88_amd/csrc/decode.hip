@@ -15,7 +15,7 @@
 // plan kernel reads context_lens on the device and cuts every sequence into parts whose length is
 // chosen from the actual lengths of the batch, so that the batch becomes about as many units of
 // equal size as the GPU holds resident waves (long sequences are split, short ones stay whole); it
-// lists the parts longest first (a counting sort on the length). A sequence of one part writes its
+// lists the parts longest first (a counting sort on the length). One wave processes a unit at a time. A sequence of one part writes its
 // output directly; otherwise each part writes an unnormalised partial (running max m, sum l,
 // accumulator o, fp32) and the reduce kernel merges them with the log-sum-exp rule.
 //
@@ -587,8 +587,8 @@ struct MfmaTile<true> {
     bool live[2];
 };
 
-// The same units on the matrix cores (bf16, head_dim 128, block_size >= 16), with a persistent grid:
-// one workgroup of one wave per resident wave slot, each taking units from the list until it is done.
+// The same units on the matrix cores (bf16, head_dim 128, block_size >= 16), with a persistent grid of
+// one workgroup per compute unit whose waves take units from the list until it is done (see the kernel).
 // The G query heads of the kv head are the N = 16 columns of v_mfma_f32_16x16x32_bf16 (columns past
 // G carry zero queries and are never written), so a 32-token tile costs 8 MFMAs per product and the
 // vector ALU keeps only the softmax.
