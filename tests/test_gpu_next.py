@@ -166,3 +166,98 @@ def test_decode_step_in_hip_graph(pkv, orc):
         orc.store(c.dtype, c.key, c.value, kh, vh, c.slot_mapping)
         ref = orc.decode(c.dtype, qn, kh, vh, c.block_tables, lens, c.scale)
         assert_close(got, ref, c.dtype, f"replay {rep}")
+
+
+def _replays_match_eager(step, refresh, outs, reps=4):
+    """Capture `step` once, then for each replay: refresh the captured inputs, replay, and compare every
+    output with an eager run of `step` on the same inputs (bit for bit)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                       # warm up on the capture stream
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(reps):
+        refresh(rep)
+        g.replay()
+        torch.cuda.synchronize()
+        replayed = [o.clone() for o in outs]
+        step()
+        torch.cuda.synchronize()
+        for a, b in zip(replayed, outs):
+            assert torch.isfinite(a.float()).all(), f"replay {rep}: non-finite output"
+            assert torch.equal(a, b), f"replay {rep} differs from eager"
+
+
+def test_fp8_decode_step_in_hip_graph(pkv):
+    """fp8 store + fp8 decode captured once and replayed with new queries and context lengths: the plan
+    kernel and the decode kernel's unit counter reset on the device, so every replay equals eager."""
+    c = W.make_decode_case("graph_fp8", 6, W.BF16, [700, 33, 1300, 512, 9, 2047], 32, 8, 128, 16, 400)
+    kr, vr, slots = W.cached_rows(c.pool)
+    shape = (c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
+    kc = torch.zeros(shape, dtype=torch.uint8, device="cuda")
+    vc = torch.zeros_like(kc)
+    ks = torch.zeros(shape[:3], dtype=torch.float32, device="cuda")
+    vs = torch.zeros_like(ks)
+    pkv.kv_cache_store_fp8(to_torch(kr, c.dtype), to_torch(vr, c.dtype), kc, vc, ks, vs, i32(slots))
+    q = to_torch(c.query, c.dtype)
+    kn, vn = to_torch(c.key, c.dtype), to_torch(c.value, c.dtype)
+    bt, cl, sm = i32(c.block_tables), i32(c.context_lens), i32(c.slot_mapping)
+    out = torch.empty_like(q)
+    ws = torch.empty(pkv.decode_workspace_size(c.num_seqs, 32, 8, 128, 16, 2048), dtype=torch.uint8, device="cuda")
+
+    def step():
+        pkv.kv_cache_store_fp8(kn, vn, kc, vc, ks, vs, sm)
+        pkv.paged_attention_decode_fp8(out, q, kc, vc, ks, vs, bt, cl, 2048, c.scale, workspace=ws)
+
+    rng = np.random.default_rng(1)
+
+    def refresh(rep):
+        q.copy_(to_torch(W._draw_values(rng, q.shape, c.dtype), c.dtype))
+        lens = np.minimum(c.context_lens, rng.integers(1, 2048, c.num_seqs)).astype(np.int32)
+        lens[rep % c.num_seqs] = c.context_lens[rep % c.num_seqs]
+        cl.copy_(i32(lens))
+
+    _replays_match_eager(step, refresh, [out])
+
+
+@pytest.mark.parametrize("kind", ["bf16", "int8"])
+def test_prefill_step_in_hip_graph(pkv, kind):
+    """Chunk store + chunked prefill captured once and replayed with new queries and chunk K/V: every replay
+    equals eager (bf16 cache, and an int8 cache)."""
+    c = W.make_prefill_case("graph_pf", 7, W.BF16, [0, 300, 1000], [70, 129, 33], 32, 8, 128, 64, 64)
+    q = to_torch(c.query, c.dtype)
+    kn, vn = to_torch(c.key, c.dtype), to_torch(c.value, c.dtype)
+    bt, cq, ck, sm = i32(c.block_tables), i32(c.cu_seqlens_q), i32(c.cu_seqlens_k), i32(c.slot_mapping)
+    out = torch.empty_like(q)
+    if kind == "bf16":
+        kc, vc = device_pool(c.pool)
+
+        def step():
+            pkv.kv_cache_store(kn, vn, kc, vc, sm)
+            pkv.paged_attention_prefill(out, q, kc, vc, bt, cq, ck, c.max_seqlen_q, c.max_seqlen_k, c.scale)
+    else:
+        kr, vr, slots = W.cached_rows(c.pool)
+        shape = (c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
+        kc = torch.zeros(shape, dtype=torch.int8, device="cuda")
+        vc = torch.zeros_like(kc)
+        ks = torch.zeros(shape[:3], dtype=torch.float32, device="cuda")
+        vs = torch.zeros_like(ks)
+        pkv.kv_cache_store_int8(to_torch(kr, c.dtype), to_torch(vr, c.dtype), kc, vc, ks, vs, i32(slots))
+
+        def step():
+            pkv.kv_cache_store_int8(kn, vn, kc, vc, ks, vs, sm)
+            pkv.paged_attention_prefill_int8(out, q, kc, vc, ks, vs, bt, cq, ck, c.max_seqlen_q, c.max_seqlen_k,
+                                             c.scale)
+
+    rng = np.random.default_rng(2)
+
+    def refresh(rep):
+        q.copy_(to_torch(W._draw_values(rng, q.shape, c.dtype), c.dtype))
+        kn.copy_(to_torch(W._draw_values(rng, kn.shape, c.dtype), c.dtype))
+        vn.copy_(to_torch(W._draw_values(rng, vn.shape, c.dtype), c.dtype))
+
+    _replays_match_eager(step, refresh, [out])
