@@ -361,6 +361,11 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_ms = np.array([ev0[k].elapsed_time(ev1[k]) for k in sampled])
     dec_avg_ms = float(dec_ms.mean())
+    def dist(x):
+        return {"mean": round(float(x.mean()), 5), "median": round(float(np.median(x)), 5),
+                "p10": round(float(np.percentile(x, 10)), 5), "p90": round(float(np.percentile(x, 90)), 5)}
+    achieved = decode_bytes(c) / (dec_avg_ms * 1e-3) / 1e9
+    finite = bool(torch.isfinite(out.float()).all().item())
     # store alone (untimed pass): events around each store
     st0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     st1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -371,12 +376,31 @@ def main():
         st1[k].record(stream)
     torch.cuda.synchronize()
     store_ms = np.array([a.elapsed_time(b) for a, b in zip(st0, st1)])
+    # the same decode in two halves (untimed pass): one plan, then runs from it, as a model's layers would
+    # (a second, identical plan halfway is timed: queued behind a run, its events measure the GPU alone)
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    r1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
-    def dist(x):
-        return {"mean": round(float(x.mean()), 5), "median": round(float(np.median(x)), 5),
-                "p10": round(float(np.percentile(x, 10)), 5), "p90": round(float(np.percentile(x, 90)), 5)}
-    achieved = decode_bytes(c) / (dec_avg_ms * 1e-3) / 1e9
-    finite = bool(torch.isfinite(out.float()).all().item())
+    def plan():
+        pkv.paged_attention_decode_plan(cl, c.max_context_len, c.num_heads, c.num_kv_heads, c.head_dim,
+                                        c.block_size, ws, dtype=td, stream=stream)
+
+    plan()
+    for k in range(args.steps):
+        kc, vc = pools[k % copies]
+        r0[k].record(stream)
+        pkv.paged_attention_decode_run(out, q, kc, vc, bt, c.max_context_len, c.scale, ws, stream=stream)
+        r1[k].record(stream)
+        if k == args.steps // 2:
+            p0.record(stream)
+            plan()
+            p1.record(stream)
+    torch.cuda.synchronize()
+    plan_run = {"plan_ms": round(p0.elapsed_time(p1), 5),
+                "run_ms": dist(np.array([a.elapsed_time(b) for a, b in zip(r0, r1)])),
+                "what": "paged_attention_decode_plan once, then paged_attention_decode_run per call (untimed pass)"}
+
 
     result = {
         "metric": "paged decode attention achieved HBM GB/s (% of peak) and decode tokens/s",
@@ -399,6 +423,7 @@ def main():
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(c.num_seqs / (ms_per_step * 1e-3), 1),
         "step_bytes": step_bytes,
+        "plan_and_runs": plan_run,
         "timing_ms": {"decode_call": dist(dec_ms), "store": dist(store_ms),
                       "events": f"HIP events on the launch stream: decode call on every {EVERY}th timed step "
                                 f"({len(sampled)} calls), store in an untimed pass after the timed steps"},

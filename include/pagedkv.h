@@ -11,7 +11,10 @@
  *   pkv_kv_cache_store_int8, pkv_paged_attention_decode_int8, pkv_paged_attention_prefill_int8:
  *                               the same over an int8 cache;
  *   pkv_kv_cache_store_fp8, pkv_paged_attention_decode_fp8, pkv_paged_attention_prefill_fp8:
- *                               the same over an fp8 (E4M3) cache.
+ *                               the same over an fp8 (E4M3) cache;
+ *   pkv_paged_attention_decode_plan and pkv_paged_attention_decode_run (_int8_run, _fp8_run):
+ *                               a decode call in two halves, the work list built once per step
+ *                               and reused by every layer's attention.
  *
  * Vocabulary (nano-vllm walkthrough, section 2 context: is_prefill, cu_seqlens_q/k, max_seqlen_q/k,
  * slot_mapping, context_lens, block_tables; "推理运行时", section 分页 KV: logical block j of a
@@ -59,6 +62,8 @@ extern "C" {
 #endif
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+/* The cache a decode plan is made for: elements of the query's dtype, int8 codes or E4M3 codes. */
+typedef enum { PKV_CACHE_ELEMENTS = 0, PKV_CACHE_INT8 = 1, PKV_CACHE_FP8 = 2 } pkv_cache_kind;
 
 typedef enum {
     PKV_OK = 0,
@@ -262,6 +267,53 @@ pkv_status pkv_paged_attention_prefill_fp8(pkv_dtype dtype, void *out, const voi
                                            int32_t max_seqlen_k, int32_t num_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
                                            int32_t causal, hipStream_t stream);
+
+/*
+ * paged_attention_decode_plan / paged_attention_decode_run: one decode call in two halves. A model runs
+ * the same attention metadata (context_lens, block_tables) through every layer of a step (nano-vllm
+ * walkthrough, section 2 context: the context is set once per forward pass and read by each layer's
+ * attention), so the work list that pkv_paged_attention_decode builds from context_lens on every call can
+ * be built once: pkv_paged_attention_decode_plan writes it into `workspace`; each
+ * pkv_paged_attention_decode_run (or _int8_run / _fp8_run over an 8-bit cache) then decodes from it and
+ * writes out, exactly as the whole call would (bit-identical results).
+ * plan: context_lens (device int32 [num_seqs]) and the sizes a run will use; cache_kind is the cache the runs
+ *   read (PKV_CACHE_ELEMENTS: the query's dtype; PKV_CACHE_INT8 / _FP8: an 8-bit cache, which needs a
+ *   bf16 query, head_dim 128 and block_size >= 16), which sizes the parts for that kernel. Errors as for
+ *   pkv_paged_attention_decode (no cache or output pointers are taken).
+ * run: the arguments of pkv_paged_attention_decode (or of its _int8 / _fp8 form) without context_lens. It
+ *   needs a workspace planned with the same num_seqs, max_context_len, num_heads, num_kv_heads, head_dim,
+ *   block_size and context_lens (the caller's contract: the work list records token ranges; a run over a
+ *   stale plan attends over the planned lengths), and reads the plan in stream order. A whole decode call
+ *   leaves the same plan in its workspace.
+ * Source: the attention metadata of the pages above, built once per step; the work list as for
+ * pkv_paged_attention_decode.
+ */
+pkv_status pkv_paged_attention_decode_plan(pkv_dtype dtype, int32_t cache_kind, const int32_t *context_lens,
+                                           int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+pkv_status pkv_paged_attention_decode_run(pkv_dtype dtype, void *out, const void *query, const void *key_cache,
+                                          const void *value_cache, const int32_t *block_tables,
+                                          int32_t block_table_stride, int32_t num_seqs, int32_t max_context_len,
+                                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int64_t num_blocks, float scale, void *workspace,
+                                          size_t workspace_bytes, hipStream_t stream);
+pkv_status pkv_paged_attention_decode_int8_run(pkv_dtype dtype, void *out, const void *query,
+                                               const int8_t *key_cache, const int8_t *value_cache,
+                                               const float *key_scale, const float *value_scale,
+                                               const int32_t *block_tables, int32_t block_table_stride,
+                                               int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                               int64_t num_blocks, float scale, void *workspace,
+                                               size_t workspace_bytes, hipStream_t stream);
+pkv_status pkv_paged_attention_decode_fp8_run(pkv_dtype dtype, void *out, const void *query,
+                                              const uint8_t *key_cache, const uint8_t *value_cache,
+                                              const float *key_scale, const float *value_scale,
+                                              const int32_t *block_tables, int32_t block_table_stride,
+                                              int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                              int64_t num_blocks, float scale, void *workspace,
+                                              size_t workspace_bytes, hipStream_t stream);
 
 /* Message of the calling thread's last non-OK status ("" if none). Owned by the library. */
 const char *pkv_last_error(void);

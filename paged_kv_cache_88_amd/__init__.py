@@ -53,6 +53,13 @@ def load_library(path: str = LIB_PATH):
         "pkv_kv_cache_store_fp8": [ctypes.c_int, P, P, P, P, P, P, P, I64, I32, I32, I32, I64, P],
         "pkv_paged_attention_decode_fp8": [ctypes.c_int, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32,
                                            I64, F, P, SZ, P],
+        "pkv_paged_attention_decode_plan": [ctypes.c_int, I32, P, I32, I32, I32, I32, I32, I32, P, SZ, P],
+        "pkv_paged_attention_decode_run": [ctypes.c_int, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I64, F, P,
+                                           SZ, P],
+        "pkv_paged_attention_decode_int8_run": [ctypes.c_int, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
+                                                I64, F, P, SZ, P],
+        "pkv_paged_attention_decode_fp8_run": [ctypes.c_int, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
+                                               I64, F, P, SZ, P],
         "pkv_paged_attention_prefill_int8": [ctypes.c_int, P, P, P, P, P, P, P, I32, P, P, I32, I32, I32, I32, I32,
                                              I32, I32, I64, F, I32, P],
         "pkv_paged_attention_prefill_fp8": [ctypes.c_int, P, P, P, P, P, P, P, I32, P, P, I32, I32, I32, I32, I32,
@@ -200,6 +207,50 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
                                           _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+_CACHE_KINDS = {"elements": 0, "int8": 1, "fp8": 2}
+
+
+def paged_attention_decode_plan(context_lens, max_context_len, num_heads, num_kv_heads, head_dim, block_size,
+                                workspace, dtype=torch.bfloat16, cache="elements", stream=None):
+    """Build a decode work list from ``context_lens`` (int32 [B]) into ``workspace`` (uint8, device, at least
+    ``decode_workspace_size(...)`` bytes), for later ``paged_attention_decode_run`` (``cache="elements"``, the
+    query's ``dtype``) or ``paged_attention_decode_int8_run`` / ``_fp8_run`` (``cache="int8"`` / ``"fp8"``)."""
+    lib = load_library()
+    _dev(context_lens, workspace)
+    _i32(context_lens)
+    if cache not in _CACHE_KINDS:
+        raise ValueError(f"cache must be one of {sorted(_CACHE_KINDS)}")
+    code = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}.get(dtype)
+    if code is None:
+        raise ValueError(f"unsupported dtype {dtype} (float32 or bfloat16)")
+    b = context_lens.shape[0]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.pkv_paged_attention_decode_plan(code, _CACHE_KINDS[cache], _ptr(context_lens), b,
+                                               int(max_context_len), int(num_heads), int(num_kv_heads),
+                                               int(head_dim), int(block_size), _ptr(workspace), ws_bytes,
+                                               _stream(stream)))
+
+
+def paged_attention_decode_run(out, query, key_cache, value_cache, block_tables, max_context_len, scale, workspace,
+                               stream=None):
+    """``paged_attention_decode`` from a work list made by ``paged_attention_decode_plan`` (same batch,
+    sizes and context lengths); ``context_lens`` is not read again."""
+    lib = load_library()
+    _dev(out, query, key_cache, value_cache, block_tables, workspace)
+    _i32(block_tables)
+    nb, hkv, bs, d = key_cache.shape
+    b, hq, d2 = query.shape
+    if d2 != d or out.shape != query.shape or value_cache.shape != key_cache.shape:
+        raise ValueError("query/out must be [B, Hq, D] with the caches' D")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b:
+        raise ValueError("block_tables must be [B, stride]")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.pkv_paged_attention_decode_run(_dtype_code(query), _ptr(out), _ptr(query), _ptr(key_cache),
+                                              _ptr(value_cache), _ptr(block_tables), block_tables.shape[1], b,
+                                              int(max_context_len), hq, hkv, d, bs, nb, float(scale), _ptr(workspace),
+                                              ws_bytes, _stream(stream)))
+
+
 _CODE_DTYPES = {"int8": (torch.int8,), "fp8": (torch.uint8, torch.float8_e4m3fn)}
 
 
@@ -248,6 +299,43 @@ def _decode_q8(kind, out, query, key_cache, value_cache, key_scale, value_scale,
     _check(fn(_dtype_code(query), _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(key_scale),
               _ptr(value_scale), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), b,
               int(max_context_len), hq, hkv, d, bs, nb, float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def _decode_q8_run(kind, out, query, key_cache, value_cache, key_scale, value_scale, block_tables,
+                   max_context_len, scale, workspace, stream):
+    lib = load_library()
+    _dev(out, query, key_cache, value_cache, key_scale, value_scale, block_tables, workspace)
+    _i32(block_tables)
+    nb, hkv, bs, d = key_cache.shape
+    b, hq, d2 = query.shape
+    if d2 != d or out.shape != query.shape or value_cache.shape != key_cache.shape:
+        raise ValueError("query/out must be [B, Hq, D] with the caches' D")
+    if key_scale.shape != (nb, hkv, bs) or value_scale.shape != (nb, hkv, bs):
+        raise ValueError("scales must be [NB, Hkv, bs]")
+    if key_cache.dtype not in _CODE_DTYPES[kind] or value_cache.dtype not in _CODE_DTYPES[kind] \
+            or key_scale.dtype != torch.float32 or value_scale.dtype != torch.float32:
+        raise ValueError(f"{kind} caches and float32 scales expected")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b:
+        raise ValueError("block_tables must be [B, stride]")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    fn = lib.pkv_paged_attention_decode_int8_run if kind == "int8" else lib.pkv_paged_attention_decode_fp8_run
+    _check(fn(_dtype_code(query), _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(key_scale),
+              _ptr(value_scale), _ptr(block_tables), block_tables.shape[1], b, int(max_context_len), hq, hkv, d, bs,
+              nb, float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def paged_attention_decode_int8_run(out, query, key_cache, value_cache, key_scale, value_scale, block_tables,
+                                    max_context_len, scale, workspace, stream=None):
+    """``paged_attention_decode_int8`` from a work list made by ``paged_attention_decode_plan(cache="int8")``."""
+    _decode_q8_run("int8", out, query, key_cache, value_cache, key_scale, value_scale, block_tables,
+                   max_context_len, scale, workspace, stream)
+
+
+def paged_attention_decode_fp8_run(out, query, key_cache, value_cache, key_scale, value_scale, block_tables,
+                                   max_context_len, scale, workspace, stream=None):
+    """``paged_attention_decode_fp8`` from a work list made by ``paged_attention_decode_plan(cache="fp8")``."""
+    _decode_q8_run("fp8", out, query, key_cache, value_cache, key_scale, value_scale, block_tables,
+                   max_context_len, scale, workspace, stream)
 
 
 def kv_cache_store_int8(key, value, key_cache, value_cache, key_scale, value_scale, slot_mapping, stream=None):

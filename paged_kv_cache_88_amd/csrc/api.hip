@@ -204,12 +204,17 @@ size_t pkv_paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_h
 
 namespace {
 
-// Validation and argument set-up shared by the decode entry points.
+// Validation and argument set-up shared by the decode entry points. A whole call (DECODE_CALL) needs every
+// pointer; a plan (DECODE_PLAN_ONLY) only context_lens and the workspace; a run (DECODE_RUN_ONLY) everything
+// but context_lens, which its plan already read.
+enum DecodeMode { DECODE_CALL, DECODE_PLAN_ONLY, DECODE_RUN_ONLY };
+
 pkv_status decode_args(pkv::DecodeArgs &a, pkv_dtype dtype, void *out, const void *query,
                        const void *key_cache, const void *value_cache, const int32_t *block_tables,
                        int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
                        int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                       int32_t block_size, int64_t num_blocks, float scale, void *workspace, size_t workspace_bytes) {
+                       int32_t block_size, int64_t num_blocks, float scale, void *workspace, size_t workspace_bytes,
+                       DecodeMode mode = DECODE_CALL) {
     pkv_status st = check_common(dtype, num_kv_heads, head_dim, block_size, num_blocks);
     if (st != PKV_OK) return st;
     st = check_heads(num_heads, num_kv_heads);
@@ -223,10 +228,13 @@ pkv_status decode_args(pkv::DecodeArgs &a, pkv_dtype dtype, void *out, const voi
     REQUIRE(isfinite(scale), PKV_EINVAL, "scale must be finite");
     REQUIRE(num_blocks > 0 || max_context_len == 0, PKV_EINVAL, "empty pool with a non-empty context");
     if (num_seqs == 0) return ok();
-    REQUIRE(out && query && key_cache && value_cache && context_lens, PKV_EINVAL, "null pointer argument");
-    REQUIRE(block_tables || max_context_len == 0, PKV_EINVAL, "null block_tables");
-    REQUIRE(aligned16(out) && aligned16(query) && aligned16(key_cache) && aligned16(value_cache), PKV_EINVAL,
-            "out, query and cache pointers must be 16-byte aligned");
+    REQUIRE(context_lens || mode == DECODE_RUN_ONLY, PKV_EINVAL, "null context_lens");
+    if (mode != DECODE_PLAN_ONLY) {
+        REQUIRE(out && query && key_cache && value_cache, PKV_EINVAL, "null pointer argument");
+        REQUIRE(block_tables || max_context_len == 0, PKV_EINVAL, "null block_tables");
+        REQUIRE(aligned16(out) && aligned16(query) && aligned16(key_cache) && aligned16(value_cache), PKV_EINVAL,
+                "out, query and cache pointers must be 16-byte aligned");
+    }
     DecodePlan plan = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len);
     REQUIRE((int64_t)num_seqs * (((int64_t)max_context_len + 31) / 32) < ((int64_t)1 << 30), PKV_EINVAL,
             "num_seqs * max_context_len too large (at most 2^35 tokens)");
@@ -261,6 +269,7 @@ pkv_status decode_args(pkv::DecodeArgs &a, pkv_dtype dtype, void *out, const voi
     a.ws_m = (float *)((char *)workspace + plan.off_m);
     a.ws_l = (float *)((char *)workspace + plan.off_l);
     a.ws_o = (float *)((char *)workspace + plan.off_o);
+    a.run_only = mode == DECODE_RUN_ONLY;
     return ok();
 }
 
@@ -314,14 +323,14 @@ pkv_status decode_q8(bool fp8, const char *what, pkv_dtype dtype, void *out, con
                      const float *value_scale, const int32_t *block_tables, int32_t block_table_stride,
                      const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
-                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                     void *workspace, size_t workspace_bytes, hipStream_t stream, DecodeMode mode = DECODE_CALL) {
     REQUIRE(dtype == PKV_BF16, PKV_EUNSUPPORTED, "8-bit-cache decode takes a bf16 query (got dtype %d)", (int)dtype);
     REQUIRE(head_dim == 128, PKV_EUNSUPPORTED, "8-bit-cache decode supports head_dim 128 (got %d)", head_dim);
     REQUIRE(block_size >= 16, PKV_EUNSUPPORTED, "8-bit-cache decode needs block_size >= 16 (got %d)", block_size);
     pkv::DecodeArgs a{};
     pkv_status st = decode_args(a, dtype, out, query, key_cache, value_cache, block_tables, block_table_stride,
                                 context_lens, num_seqs, max_context_len, num_heads, num_kv_heads, head_dim, block_size,
-                                num_blocks, scale, workspace, workspace_bytes);
+                                num_blocks, scale, workspace, workspace_bytes, mode);
     if (st != PKV_OK || num_seqs == 0) return st;
     REQUIRE(key_scale && value_scale, PKV_EINVAL, "null scale array");
     REQUIRE(((uintptr_t)key_scale & 15u) == 0 && ((uintptr_t)value_scale & 15u) == 0, PKV_EINVAL,
@@ -376,6 +385,72 @@ pkv_status pkv_paged_attention_decode_fp8(pkv_dtype dtype, void *out, const void
                      key_scale, value_scale, block_tables, block_table_stride, context_lens, num_seqs,
                      max_context_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace,
                      workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_attention_decode_plan(pkv_dtype dtype, int32_t cache_kind, const int32_t *context_lens,
+                                           int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    REQUIRE(cache_kind == PKV_CACHE_ELEMENTS || cache_kind == PKV_CACHE_INT8 || cache_kind == PKV_CACHE_FP8,
+            PKV_EINVAL, "cache_kind %d is not PKV_CACHE_ELEMENTS, _INT8 or _FP8", cache_kind);
+    const bool q8 = cache_kind != PKV_CACHE_ELEMENTS;
+    if (q8) {
+        REQUIRE(dtype == PKV_BF16, PKV_EUNSUPPORTED, "8-bit-cache decode takes a bf16 query (got dtype %d)",
+                (int)dtype);
+        REQUIRE(head_dim == 128, PKV_EUNSUPPORTED, "8-bit-cache decode supports head_dim 128 (got %d)", head_dim);
+        REQUIRE(block_size >= 16, PKV_EUNSUPPORTED, "8-bit-cache decode needs block_size >= 16 (got %d)", block_size);
+    }
+    pkv::DecodeArgs a{};
+    const pkv_status st = decode_args(a, dtype, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                      (max_context_len + block_size - 1) / (block_size > 0 ? block_size : 1),
+                                      context_lens, num_seqs, max_context_len, num_heads, num_kv_heads, head_dim,
+                                      block_size, 1, 1.0f, workspace, workspace_bytes, DECODE_PLAN_ONLY);
+    if (st != PKV_OK || num_seqs == 0) return st;
+    const bool mfma = q8 || pkv::decode_uses_mfma(dtype == PKV_BF16, head_dim, num_heads / num_kv_heads, a.log2_bs);
+    return hip_status(pkv::launch_decode_plan(a, mfma, q8, stream), "paged_attention_decode_plan launch");
+}
+
+pkv_status pkv_paged_attention_decode_run(pkv_dtype dtype, void *out, const void *query, const void *key_cache,
+                                          const void *value_cache, const int32_t *block_tables,
+                                          int32_t block_table_stride, int32_t num_seqs, int32_t max_context_len,
+                                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int64_t num_blocks, float scale, void *workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+    pkv::DecodeArgs a{};
+    const pkv_status st = decode_args(a, dtype, out, query, key_cache, value_cache, block_tables, block_table_stride,
+                                      nullptr, num_seqs, max_context_len, num_heads, num_kv_heads, head_dim, block_size,
+                                      num_blocks, scale, workspace, workspace_bytes, DECODE_RUN_ONLY);
+    if (st != PKV_OK || num_seqs == 0) return st;
+    return hip_status(pkv::launch_decode(a, dtype == PKV_BF16, head_dim, num_heads / num_kv_heads, stream),
+                      "paged_attention_decode_run launch");
+}
+
+pkv_status pkv_paged_attention_decode_int8_run(pkv_dtype dtype, void *out, const void *query,
+                                               const int8_t *key_cache, const int8_t *value_cache,
+                                               const float *key_scale, const float *value_scale,
+                                               const int32_t *block_tables, int32_t block_table_stride,
+                                               int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                               int64_t num_blocks, float scale, void *workspace,
+                                               size_t workspace_bytes, hipStream_t stream) {
+    return decode_q8(false, "paged_attention_decode_int8_run launch", dtype, out, query, key_cache, value_cache,
+                     key_scale, value_scale, block_tables, block_table_stride, nullptr, num_seqs, max_context_len,
+                     num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace, workspace_bytes,
+                     stream, DECODE_RUN_ONLY);
+}
+
+pkv_status pkv_paged_attention_decode_fp8_run(pkv_dtype dtype, void *out, const void *query,
+                                              const uint8_t *key_cache, const uint8_t *value_cache,
+                                              const float *key_scale, const float *value_scale,
+                                              const int32_t *block_tables, int32_t block_table_stride,
+                                              int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                              int64_t num_blocks, float scale, void *workspace,
+                                              size_t workspace_bytes, hipStream_t stream) {
+    return decode_q8(true, "paged_attention_decode_fp8_run launch", dtype, out, query, key_cache, value_cache,
+                     key_scale, value_scale, block_tables, block_table_stride, nullptr, num_seqs, max_context_len,
+                     num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace, workspace_bytes,
+                     stream, DECODE_RUN_ONLY);
 }
 
 }  // extern "C"

@@ -125,7 +125,7 @@ __device__ int plan_exclusive_scan(int v, int *s_wave, int *total) {
 // items[k] = {seq, first token, tokens, partial slot (-1 when the sequence is one part)}, longest first
 // (64-bucket counting sort; order inside a bucket is arbitrary and every unit writes its own output, so
 // results do not depend on it). seq_info[i] = {first partial slot, n_i, len_i, L_i}; ctrl[0] = number of
-// parts. Sequences with L_i = 0 get zero outputs here. One workgroup; thread t owns sequences
+// parts (sequences with L_i = 0 have no parts; the reduce kernel writes their zero outputs). One workgroup; thread t owns sequences
 // t + k * PLAN_THREADS, and keeps the first PLAN_REG of them in registers (larger batches re-read
 // seq_info).
 constexpr int PLAN_REG = 4;
@@ -133,8 +133,7 @@ constexpr int PLAN_REG = 4;
 __global__ void __launch_bounds__(PLAN_THREADS)
 decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int max_context_len, int num_kv_heads,
                    int workers, int min_strata, int max_tiles, int min_tiles,
-                   int4 *__restrict__ items, int4 *__restrict__ seq_info,
-                   int *__restrict__ ctrl, void *__restrict__ out, int out_row_elems, int elem_bytes) {
+                   int4 *__restrict__ items, int4 *__restrict__ seq_info, int *__restrict__ ctrl) {
     __shared__ int s_wave[PLAN_WAVES];
     __shared__ int hist[PLAN_BUCKETS];
     __shared__ int offs[PLAN_BUCKETS];
@@ -217,13 +216,7 @@ decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int m
                 if (r == k) sreg[r] = si;
             if (i < num_seqs) {
                 seq_info[i] = si;
-                if (n > 0) {
-                    my_max = max(my_max, min(len, L));
-                } else {                              // empty context: zero outputs for every head
-                    const int64_t words = (int64_t)out_row_elems * elem_bytes / 4;
-                    uint32_t *o = (uint32_t *)((char *)out + (int64_t)i * out_row_elems * elem_bytes);
-                    for (int64_t w = 0; w < words; ++w) o[w] = 0u;
-                }
+                if (n > 0) my_max = max(my_max, min(len, L));
             }
             carry += chunk;
         }
@@ -968,7 +961,7 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
 // workgroups exit after one load). Its threads are hpb heads x PL = 8 / hpb part lanes x D/4 dim groups:
 // a thread merges dims 4 dg .. +4 of the parts p = pl mod PL with 16-byte loads (running max, so each
 // part's m, l, o load in one round trip), and the part lanes are merged through LDS by the same rule.
-// Sequences of one part were written by the decode kernel.
+// Sequences of one part were written by the decode kernel; empty ones get zeros here.
 constexpr int REDUCE_THREADS = 256;
 
 template <bool BF16, int D>
@@ -981,7 +974,16 @@ decode_reduce_kernel(void *__restrict__ out, const int4 *__restrict__ seq_info, 
     const int seq = blockIdx.y;
     const int4 si = seq_info[seq];
     const int nparts = si.y;
-    if (nparts <= 1) return;
+    if (nparts == 0) {                           // empty context: zero outputs for this workgroup's heads
+        const int h0 = blockIdx.x * hpb, nh = min(hpb, num_heads - h0);
+        const int64_t base = ((int64_t)seq * num_heads + h0) * D;
+        for (int e = threadIdx.x; e < nh * D; e += REDUCE_THREADS) {
+            if constexpr (BF16) ((uint16_t *)out)[base + e] = 0;
+            else ((float *)out)[base + e] = 0.f;
+        }
+        return;
+    }
+    if (nparts == 1) return;
     const int PL = SLOTS / hpb;
     const int t = threadIdx.x, slot = t / DG, dg = t % DG;
     const int hs = slot / PL, pl = slot % PL;
@@ -1029,17 +1031,25 @@ decode_reduce_kernel(void *__restrict__ out, const int4 *__restrict__ seq_info, 
     }
 }
 
+// The plan kernel, sizing parts for the resident waves of the decode kernel that will run: the matrix-core
+// kernel runs one workgroup of DECODE_CU_WAVES_BF16 / _Q8 waves per compute unit, the other a.workers.
+static hipError_t launch_plan(const DecodeArgs &a, bool mfma, bool q8, hipStream_t stream) {
+    const int workers = mfma ? a.compute_units * (q8 ? DECODE_CU_WAVES_Q8 : DECODE_CU_WAVES_BF16) : a.workers;
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, a.context_lens, a.num_seqs,
+                       a.max_context_len, a.num_kv_heads, workers, a.min_strata, a.max_part_tiles, a.min_part_tiles,
+                       a.items, a.seq_info, a.ctrl);
+    return hipGetLastError();
+}
+
 template <bool BF16, int D, int G, int NV, int R, int NW, bool MFMA>
 static hipError_t launch_decode_cfg(const DecodeArgs &a, hipStream_t stream) {
-    // resident waves the plan sizes parts for: the matrix-core kernel runs NWV waves per compute unit
     const bool q8 = a.key_scale != nullptr;
     const int nwv = q8 ? DECODE_CU_WAVES_Q8 : DECODE_CU_WAVES_BF16;
-    const int workers = MFMA ? a.compute_units * nwv : a.workers;
-    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, a.context_lens, a.num_seqs,
-                       a.max_context_len, a.num_kv_heads, workers, a.min_strata, a.max_part_tiles,
-                       a.min_part_tiles, a.items, a.seq_info, a.ctrl, a.out, a.num_kv_heads * G * D, BF16 ? 2 : 4);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (!a.run_only) {
+        e = launch_plan(a, MFMA, q8, stream);
+        if (e != hipSuccess) return e;
+    }
     const int64_t units = (int64_t)a.max_items * a.num_kv_heads;     // upper bound on the unit count
     if constexpr (MFMA) {
         static_assert(BF16 && D == 128, "matrix-core decode: bf16, head_dim 128");
@@ -1127,6 +1137,15 @@ hipError_t launch_decode_q8(const DecodeArgs &a, int group, hipStream_t stream) 
         case 8: return launch_decode_cfg<true, 128, 8, 1, 4, 1, true>(a, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+bool decode_uses_mfma(bool bf16, int head_dim, int group, int log2_bs) {
+    return bf16 && head_dim == 128 && group >= PKV_DECODE_MFMA_MIN_G && group <= 16 && log2_bs >= 4;
+}
+
+hipError_t launch_decode_plan(const DecodeArgs &a, bool mfma, bool q8, hipStream_t stream) {
+    if (a.num_seqs == 0) return hipSuccess;
+    return launch_plan(a, mfma, q8, stream);
 }
 
 int decode_max_part_blocks() { return MAX_PART_BLOCKS; }

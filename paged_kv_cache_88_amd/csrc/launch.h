@@ -54,11 +54,16 @@ struct DecodeArgs {
     const float *key_scale = nullptr;     // 8-bit caches only: [num_blocks][num_kv_heads][block_size]
     const float *value_scale = nullptr;
     bool fp8_codes = false;               // 8-bit caches: E4M3 codes instead of int8
+    bool run_only = false;                // decode and reduce from a work list already in the workspace
 };
 
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, int head_dim, int group, hipStream_t stream);
 // 8-bit caches (int8 or E4M3 codes + per-row scales), bf16 query and output, head_dim 128, block_size >= 16.
 hipError_t launch_decode_q8(const DecodeArgs &a, int group, hipStream_t stream);
+// The plan kernel alone (the work list a later run_only call decodes from), for the kernel that will run:
+// the matrix-core one (decode_uses_mfma, or any 8-bit cache) or not, over an 8-bit cache or not.
+hipError_t launch_decode_plan(const DecodeArgs &a, bool mfma, bool q8, hipStream_t stream);
+bool decode_uses_mfma(bool bf16, int head_dim, int group, int log2_bs);
 int decode_max_part_blocks();
 int decode_tile_tokens();
 

@@ -139,6 +139,29 @@ def test_prefill_q8_validation(lib, name):
     assert call(1, None, None, None, None, None, None, None, 4, None, None, 2, 0, 64, 8, 2, 128, 16, 64, 0.1, 1, None) == 0
 
 
+def test_decode_plan_and_run_validation(lib):
+    """The two halves of a decode call check their own arguments before any launch."""
+    plan, run = lib.pkv_paged_attention_decode_plan, lib.pkv_paged_attention_decode_run
+    need = lib.pkv_paged_attention_decode_workspace_size(2, 8, 2, 128, 16, 64)
+    ws = ctypes.c_void_p(1 << 24)
+    # (dtype, cache_kind, context_lens, B, max_len, Hq, Hkv, D, bs, workspace, bytes, stream)
+    assert plan(1, 3, FAKE, 2, 64, 8, 2, 128, 16, ws, need, None) == 1              # unknown cache kind
+    assert plan(1, 2, FAKE, 2, 64, 8, 2, 64, 16, ws, need, None) == 2               # fp8 cache needs D 128
+    assert plan(0, 1, FAKE, 2, 64, 8, 2, 128, 16, ws, need, None) == 2              # 8-bit cache needs bf16
+    assert plan(1, 0, None, 2, 64, 8, 2, 128, 16, ws, need, None) == 1              # null context_lens
+    assert plan(1, 0, FAKE, 2, 64, 8, 2, 128, 16, ws, need - 1, None) == 3          # workspace too small
+    assert plan(1, 0, None, 0, 64, 8, 2, 128, 16, None, 0, None) == 0               # no sequences: no-op
+    # (dtype, out, q, kc, vc, bt, stride, B, max_len, Hq, Hkv, D, bs, NB, scale, workspace, bytes, stream)
+    assert run(1, None, FAKE, FAKE, FAKE, FAKE, 4, 2, 64, 8, 2, 128, 16, 64, 0.1, ws, need, None) == 1
+    assert run(1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 64, 8, 2, 128, 16, 64, 0.1, None, 0, None) == 3
+    assert run(1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 65, 8, 2, 128, 16, 64, 0.1, ws, need, None) == 1   # past table
+    for name in ("pkv_paged_attention_decode_int8_run", "pkv_paged_attention_decode_fp8_run"):
+        r8 = getattr(lib, name)
+        # null scales; block size below 16
+        assert r8(1, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 2, 64, 8, 2, 128, 16, 64, 0.1, ws, need, None) == 1
+        assert r8(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2, 64, 8, 2, 128, 8, 64, 0.1, ws, need, None) == 2
+
+
 def test_binding_fails_loudly_without_library(pkv, tmp_path):
     saved = pkv._lib
     try:
