@@ -76,9 +76,12 @@ class Oracle:
         lib.orc_quantize_fp8.argtypes = [ctypes.c_int, P, I64, I32, P, P]
         lib.orc_store_fp8.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, I64, I32, I32, I32, I64]
         lib.orc_dequantize_fp8.argtypes = [P, P, I64, I32, P]
+        lib.orc_quantize_int4.argtypes = [ctypes.c_int, P, I64, I32, P, P]
+        lib.orc_store_int4.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, I64, I32, I32, I32, I64]
+        lib.orc_dequantize_int4.argtypes = [P, P, I64, I32, P]
         for f in (lib.orc_store, lib.orc_gather, lib.orc_decode, lib.orc_prefill, lib.orc_quantize_int8,
                   lib.orc_store_int8, lib.orc_dequantize_int8, lib.orc_quantize_fp8, lib.orc_store_fp8,
-                  lib.orc_dequantize_fp8):
+                  lib.orc_dequantize_fp8, lib.orc_quantize_int4, lib.orc_store_int4, lib.orc_dequantize_int4):
             f.restype = ctypes.c_int
         lib.orc_last_error.restype = ctypes.c_char_p
         lib.orc_max_threads.restype = ctypes.c_int
@@ -187,6 +190,49 @@ class Oracle:
             raise ValueError("one scale per row")
         out = np.empty(c.shape, dtype=np.float64)
         self._check(self.lib.orc_dequantize_fp8(_ptr(c), _ptr(sc), c.size // d, d, _ptr(out)))
+        return out
+
+    def quantize_int4(self, dtype, rows):
+        """4-bit codes and float32 scales of rows ``[..., D]`` (D even; one scale per row): scale = max|x| / 7,
+        q = round-half-even(x / scale) clamped to [-7, 7], in float32, stored as u = q + 8 two per byte (element
+        2j in the low four bits of byte j): codes ``[..., D / 2]`` uint8; zero rows give scale 0 and u = 8."""
+        sd = _store_dtype(dtype)
+        r = _c(rows, sd)
+        d = r.shape[-1]
+        n = r.size // d
+        codes = np.zeros(r.shape[:-1] + (d // 2,), dtype=np.uint8)
+        scales = np.zeros(r.shape[:-1], dtype=np.float32)
+        self._check(self.lib.orc_quantize_int4(_DT[dtype], _ptr(r), n, d, _ptr(codes), _ptr(scales)))
+        return codes, scales
+
+    def store_int4(self, dtype, key, value, key_cache, value_cache, key_scale, value_scale, slot_mapping):
+        """Quantize rows of key/value ``[N, Hkv, D]`` to 4-bit codes and scatter them into the int4 caches
+        ``[NB, Hkv, bs, D / 2]`` (uint8) and scales into ``[NB, Hkv, bs]`` float32, in place (slots as in
+        ``store``)."""
+        sd = _store_dtype(dtype)
+        for a, t in ((key_cache, np.uint8), (value_cache, np.uint8), (key_scale, np.float32), (value_scale, np.float32)):
+            if a.dtype != t or not a.flags.c_contiguous:
+                raise TypeError("int4 caches (uint8) and float32 scales must be C-contiguous")
+        key, value = _c(key, sd), _c(value, sd)
+        sm = _c(slot_mapping, np.int32)
+        nb, hkv, bs, half = key_cache.shape
+        if key.shape[-1] != 2 * half:
+            raise ValueError("int4 cache rows hold head_dim / 2 bytes")
+        if key_scale.shape != (nb, hkv, bs) or value_scale.shape != (nb, hkv, bs):
+            raise ValueError("scale arrays must be [num_blocks, num_kv_heads, block_size]")
+        self._check(self.lib.orc_store_int4(_DT[dtype], _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                            _ptr(key_scale), _ptr(value_scale), _ptr(sm), len(sm), hkv, 2 * half, bs,
+                                            nb))
+
+    def dequantize_int4(self, codes, scales):
+        """float64 values (u - 8) * scale (exact) of int4 rows ``[..., D / 2]`` bytes with scales ``[...]``:
+        returns ``[..., D]``."""
+        c, sc = _c(codes, np.uint8), _c(scales, np.float32)
+        half = c.shape[-1]
+        if sc.shape != c.shape[:-1]:
+            raise ValueError("one scale per row")
+        out = np.empty(c.shape[:-1] + (2 * half,), dtype=np.float64)
+        self._check(self.lib.orc_dequantize_int4(_ptr(c), _ptr(sc), c.size // half, 2 * half, _ptr(out)))
         return out
 
     def copy_blocks(self, dtype, key_cache, value_cache, pairs):
@@ -320,3 +366,15 @@ def store_fp8(*a, **k):
 
 def dequantize_fp8(*a, **k):
     return default().dequantize_fp8(*a, **k)
+
+
+def quantize_int4(*a, **k):
+    return default().quantize_int4(*a, **k)
+
+
+def store_int4(*a, **k):
+    return default().store_int4(*a, **k)
+
+
+def dequantize_int4(*a, **k):
+    return default().dequantize_int4(*a, **k)

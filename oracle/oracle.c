@@ -12,6 +12,8 @@
  *   int8 cache (orc_store_int8): codes [num_blocks][num_kv_heads][block_size][head_dim] int8 and one
  *   float32 scale per row, [num_blocks][num_kv_heads][block_size]
  *   fp8 cache (orc_store_fp8): the same with one-byte E4M3 codes in place of int8
+ *   int4 cache (orc_store_int4): codes [num_blocks][num_kv_heads][block_size][head_dim / 2] bytes, two 4-bit
+ *   codes per byte, and the same float32 scales
  *
  * Sources (web pages on the paged KV cache):
  *   - logical block j of a request lives in physical block block_table[j]; the kernel reads K/V
@@ -25,9 +27,9 @@
  *   - chunked prefill: a chunk attends to its cached prefix and to itself
  *     (Mini-SGLang 源码解析（二）, sections 6.6 and 6.9; "推理运行时", section Prefill 与 decode 输入);
  *   - a quantized cache keeps K/V as int8 (or another 8-bit type) instead of bf16, at some loss of
- *     accuracy ("LLM Infra 101 v0.2: KV Cache", inference-engine list, KV Quantization). The pages fix no
- *     scheme; the ones restated here are symmetric, one scale per (token, kv head) row, with int8 codes
- *     or OCP float8 E4M3 codes.
+ *     accuracy ("LLM Infra 101 v0.2: KV Cache", inference-engine list, KV Quantization, which names int8
+ *     and int4). The pages fix no scheme; the ones restated here are symmetric, one scale per (token, kv
+ *     head) row, with int8 codes, OCP float8 E4M3 codes, or 4-bit codes.
  * Attention itself is the textbook definition softmax(scale * q . k) weighted sum of v.
  */
 #include <math.h>
@@ -181,6 +183,91 @@ int orc_dequantize_int8(const int8_t *codes, const float *scales, int64_t nrows,
     if (nrows < 0 || dim <= 0) return fail("bad sizes (rows %lld, dim %d)", (long long)nrows, dim);
     for (int64_t r = 0; r < nrows; ++r)
         for (int32_t d = 0; d < dim; ++d) out[r * dim + d] = (double)codes[r * dim + d] * (double)scales[r];
+    return ORC_OK;
+}
+
+/*
+ * int4 quantization of rows of `dim` (even) elements, one scale per row, all arithmetic in float32:
+ *   a = max_d |x_d|,  scale = a / 7,  q_d = round_half_even(x_d / scale) clamped to [-7, 7];
+ * stored offset by 8, u_d = q_d + 8 in [1, 15], two codes per byte: element 2j in the low four bits of
+ * byte j, element 2j + 1 in the high four bits. A row of zeros gets scale 0 and codes u = 8 (q = 0).
+ * Dequantized, x_d ~ q_d * scale, |error| <= scale / 2. Rows must be finite.
+ */
+int orc_quantize_int4(int dtype, const void *rows, int64_t nrows, int32_t dim, uint8_t *codes, float *scales) {
+    if (dtype != 0 && dtype != 1) return fail("bad dtype %d", dtype);
+    if (nrows < 0 || dim <= 0 || dim % 2) return fail("bad sizes (rows %lld, dim %d)", (long long)nrows, dim);
+    for (int64_t r = 0; r < nrows; ++r) {
+        float amax = 0.0f;
+        for (int32_t d = 0; d < dim; ++d) {
+            float x = (float)elem(dtype, rows, r * dim + d);
+            if (!isfinite(x)) return fail("row %lld holds a non-finite value", (long long)r);
+            if (fabsf(x) > amax) amax = fabsf(x);
+        }
+        float step = amax / 7.0f;
+        scales[r] = step;
+        for (int32_t j = 0; j < dim / 2; ++j) {
+            int u[2];
+            for (int half = 0; half < 2; ++half) {
+                float q = 0.0f;
+                if (amax > 0.0f) {
+                    q = nearbyintf((float)elem(dtype, rows, r * dim + 2 * j + half) / step);
+                    q = fminf(fmaxf(q, -7.0f), 7.0f);
+                }
+                u[half] = (int)q + 8;
+            }
+            codes[r * (dim / 2) + j] = (uint8_t)(u[0] | (u[1] << 4));
+        }
+    }
+    return ORC_OK;
+}
+
+/* Store into an int4 cache: as orc_store_int8, with rows of head_dim / 2 bytes of orc_quantize_int4 codes. */
+int orc_store_int4(int dtype, const void *key, const void *value, uint8_t *key_cache, uint8_t *value_cache,
+                   float *key_scale, float *value_scale, const int32_t *slot_mapping, int64_t num_tokens,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks) {
+    if (dtype != 0 && dtype != 1) return fail("bad dtype %d", dtype);
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || head_dim % 2 || block_size <= 0 || num_blocks < 0)
+        return fail("bad sizes (tokens %lld, blocks %lld, head_dim %d)", (long long)num_tokens, (long long)num_blocks,
+                    head_dim);
+    int64_t nslots = num_blocks * block_size;
+    unsigned char *seen = (unsigned char *)calloc((size_t)(nslots > 0 ? nslots : 1), 1);
+    if (!seen) return fail("out of memory");
+    for (int64_t n = 0; n < num_tokens; ++n) {
+        int64_t s = slot_mapping[n];
+        if (s < 0) continue;
+        if (s >= nslots) { free(seen); return fail("slot %lld outside the pool of %lld slots", (long long)s, (long long)nslots); }
+        if (seen[s]) { free(seen); return fail("slot %lld written twice (token %lld)", (long long)s, (long long)n); }
+        seen[s] = 1;
+    }
+    free(seen);
+    size_t eb = elem_bytes(dtype);
+    int64_t row_bytes = head_dim / 2;
+    for (int64_t n = 0; n < num_tokens; ++n) {
+        int64_t s = slot_mapping[n];
+        if (s < 0) continue;
+        int64_t blk = s / block_size, pos = s % block_size;
+        for (int64_t h = 0; h < num_kv_heads; ++h) {
+            int64_t crow = (blk * num_kv_heads + h) * block_size + pos;
+            int64_t src = (n * num_kv_heads + h) * head_dim;
+            int rc = orc_quantize_int4(dtype, (const char *)key + src * eb, 1, head_dim,
+                                       key_cache + crow * row_bytes, key_scale + crow);
+            if (!rc) rc = orc_quantize_int4(dtype, (const char *)value + src * eb, 1, head_dim,
+                                            value_cache + crow * row_bytes, value_scale + crow);
+            if (rc) return rc;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Dequantize int4 rows: out[r][d] = (u_d - 8) * scales[r] in float64 (exact), u_d the 4-bit code of element d. */
+int orc_dequantize_int4(const uint8_t *codes, const float *scales, int64_t nrows, int32_t dim, double *out) {
+    if (nrows < 0 || dim <= 0 || dim % 2) return fail("bad sizes (rows %lld, dim %d)", (long long)nrows, dim);
+    for (int64_t r = 0; r < nrows; ++r)
+        for (int32_t d = 0; d < dim; ++d) {
+            int byte = codes[r * (dim / 2) + d / 2];
+            int u = (d % 2) ? (byte >> 4) : (byte & 15);
+            out[r * dim + d] = (double)(u - 8) * (double)scales[r];
+        }
     return ORC_OK;
 }
 

@@ -19,7 +19,11 @@ What pins what:
 * fp8 (OCP float8 E4M3) cache quantization: the format's fixed points (zero, the smallest subnormal and
   normal, one, 448, the NaN patterns), its grid structure, encoding and decoding of every code against
   torch's own ``float8_e4m3fn`` conversion (round half to even, NaN past 464), the relative error bound,
-  placement by slot, and decode on an exactly representable cache equal to decode on the float cache.
+  placement by slot, and decode on an exactly representable cache equal to decode on the float cache;
+* int4 cache quantization: a hand-encoded row (its four bytes written out from the definition: offset-8
+  codes, element 2j in the low nibble), exact cases, round-half-even ties, the half-step error bound, sign
+  symmetry (u -> 16 - u), placement by slot, and decode on an exactly quantized cache equal to decode on
+  the float cache.
 """
 from __future__ import annotations
 
@@ -482,6 +486,103 @@ def check_fp8_decode_exact_case_matches_float_decode(orc, seed=57):
     assert np.abs(got - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
 
 
+def check_int4_hand_encoded_row(orc):
+    """Row [3.5, -3.5, 0, 1, 0.25, -0.25, 1.5, 2]: absmax 3.5, scale 0.5; q = [7, -7, 0, 2, 0 (tie 0.5 to
+    even), 0 (tie -0.5), 3, 4]; u = q + 8 = [15, 1, 8, 10, 8, 8, 11, 12]; bytes (low nibble first) 0x1f,
+    0xa8, 0x88, 0xcb, worked by hand from the definition."""
+    x = np.array([[3.5, -3.5, 0.0, 1.0, 0.25, -0.25, 1.5, 2.0]], np.float32)
+    codes, scales = orc.quantize_int4(F32, x)
+    assert scales.tolist() == [0.5]
+    assert codes[0].tolist() == [0x1F, 0xA8, 0x88, 0xCB]
+    assert orc.dequantize_int4(codes, scales)[0].tolist() == [3.5, -3.5, 0.0, 1.0, 0.0, 0.0, 1.5, 2.0]
+
+
+def check_int4_power_of_two_scale(orc):
+    """Rows whose largest magnitude is 7 * 2^-2 and whose elements are integer multiples of 2^-2:
+    scale = 2^-2 exactly, q = the integers, dequantized values = the inputs."""
+    k = np.array([[-7, 5, 0, 6, -3, 4, 1, -1, 2, -6], [7, -7, 3, 0, 0, 0, 2, -2, -5, 1]], np.int64)
+    x = (k * 0.25).astype(np.float32)
+    codes, scales = orc.quantize_int4(F32, x)
+    assert np.array_equal(scales, np.full(2, 0.25, np.float32))
+    lo, hi = (codes & 15).astype(np.int64) - 8, (codes >> 4).astype(np.int64) - 8
+    assert np.array_equal(np.stack([lo, hi], axis=-1).reshape(2, -1), k)
+    assert np.array_equal(orc.dequantize_int4(codes, scales), x.astype(np.float64))
+
+
+def check_int4_ties_to_even(orc):
+    """scale 1 (absmax 7): halves round to the even integer (round-half-even), both signs."""
+    x = np.array([[7.0, 0.5, 1.5, 2.5, 3.5, -0.5, -2.5, 6.5, -3.5, 0.0]], np.float32)
+    codes, scales = orc.quantize_int4(F32, x)
+    assert scales[0] == 1.0
+    q = np.stack([(codes[0] & 15).astype(int) - 8, (codes[0] >> 4).astype(int) - 8], axis=-1).reshape(-1)
+    assert q.tolist() == [7, 0, 2, 2, 4, 0, -2, 6, -4, 0]
+
+
+def check_int4_zero_row_bound_and_symmetry(orc, seed=58):
+    """A zero row gives scale 0 and bytes 0x88 (q = 0). Random rows: |deq - x| <= scale / 2, the largest
+    magnitude maps to +-7, and negating a row maps every code u to 16 - u with the same scale."""
+    rng = np.random.default_rng(seed)
+    z_codes, z_scales = orc.quantize_int4(F32, np.zeros((1, 16), np.float32))
+    assert z_scales[0] == 0.0 and np.all(z_codes == 0x88)
+    x = (rng.standard_normal((40, 64)) * rng.uniform(0.01, 100, (40, 1))).astype(np.float32)
+    codes, scales = orc.quantize_int4(F32, x)
+    deq = orc.dequantize_int4(codes, scales)
+    assert np.all(np.abs(deq - x.astype(np.float64)) <= scales[:, None].astype(np.float64) * (0.5 + 1e-6))
+    i = np.argmax(np.abs(x), axis=1)
+    assert np.array_equal(np.abs(deq[np.arange(40), i]), 7 * scales.astype(np.float64))
+    n_codes, n_scales = orc.quantize_int4(F32, -x)
+    u = np.stack([codes & 15, codes >> 4], -1).astype(np.int64)
+    nu = np.stack([n_codes & 15, n_codes >> 4], -1).astype(np.int64)
+    assert np.array_equal(n_scales, scales) and np.array_equal(nu, 16 - u)
+
+
+def check_int4_store_places_rows(orc, seed=59):
+    """store_int4 puts each row's bytes and scale at (s // bs, head, s % bs) of the [NB, Hkv, bs(, D / 2)]
+    arrays; untouched rows keep their sentinels; negative slots write nothing."""
+    rng = np.random.default_rng(seed)
+    nb, hkv, bs, d = 5, 2, 4, 8
+    kc = np.full((nb, hkv, bs, d // 2), 0x55, np.uint8)
+    vc = np.full((nb, hkv, bs, d // 2), 0xAA, np.uint8)
+    ks = np.full((nb, hkv, bs), -1.0, np.float32)
+    vs = np.full((nb, hkv, bs), -2.0, np.float32)
+    slots = np.array([3, 17, -1, 8, 19], np.int32)
+    key = rng.standard_normal((5, hkv, d)).astype(np.float32)
+    val = (3 * rng.standard_normal((5, hkv, d))).astype(np.float32)
+    orc.store_int4(F32, key, val, kc, vc, ks, vs, slots)
+    touched = np.zeros((nb, bs), bool)
+    for n, s in enumerate(slots):
+        if s < 0:
+            continue
+        for h in range(hkv):
+            kq, ksc = orc.quantize_int4(F32, key[n, h][None])
+            vq, vsc = orc.quantize_int4(F32, val[n, h][None])
+            assert np.array_equal(kc[s // bs, h, s % bs], kq[0]) and ks[s // bs, h, s % bs] == ksc[0]
+            assert np.array_equal(vc[s // bs, h, s % bs], vq[0]) and vs[s // bs, h, s % bs] == vsc[0]
+        touched[s // bs, s % bs] = True
+    assert np.all(kc.transpose(0, 2, 1, 3)[~touched] == 0x55) and np.all(vc.transpose(0, 2, 1, 3)[~touched] == 0xAA)
+    assert np.all(ks.transpose(0, 2, 1)[~touched] == -1.0) and np.all(vs.transpose(0, 2, 1)[~touched] == -2.0)
+
+
+def check_int4_decode_exact_case_matches_float_decode(orc, seed=60):
+    """When every row is an integer multiple of a power of two with absmax 7 times it, 4-bit quantization
+    is exact, so decode over the dequantized int4 cache ("f64") equals decode over the float cache."""
+    rng = np.random.default_rng(seed)
+    nb, hkv, bs, d = 8, 2, 4, 8
+    ints = rng.integers(-7, 8, size=(nb, hkv, bs, d))
+    ints[..., 0] = np.where(rng.random((nb, hkv, bs)) < 0.5, 7, -7)
+    kf = (ints * 0.25).astype(np.float32)
+    vf = (np.roll(ints, 1, axis=-1) * 0.5).astype(np.float32)
+    kq, ks = orc.quantize_int4(F32, kf)
+    vq, vs = orc.quantize_int4(F32, vf)
+    bt = _tables(rng, [13, 5], bs, nb)
+    q = rng.standard_normal((2, 4, d)).astype(np.float32)
+    lens = np.array([13, 5], np.int32)
+    ref = orc.decode(F32, q, kf, vf, bt, lens, 0.01)
+    got = orc.decode("f64", q.astype(np.float64), orc.dequantize_int4(kq, ks), orc.dequantize_int4(vq, vs), bt, lens,
+                     0.01)
+    assert np.abs(got - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
 ALL_CHECKS = [
     check_gather_matches_numpy_indexing,
     check_single_key,
@@ -506,4 +607,10 @@ ALL_CHECKS = [
     check_fp8_zero_row_bound_and_symmetry,
     check_fp8_store_places_rows,
     check_fp8_decode_exact_case_matches_float_decode,
+    check_int4_hand_encoded_row,
+    check_int4_power_of_two_scale,
+    check_int4_ties_to_even,
+    check_int4_zero_row_bound_and_symmetry,
+    check_int4_store_places_rows,
+    check_int4_decode_exact_case_matches_float_decode,
 ]

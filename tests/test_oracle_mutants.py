@@ -71,6 +71,17 @@ MUTANTS = {
     "fp8_scale_over_240": ("float scale = a / 448.0f;", "float scale = a / 240.0f;"),
     "fp8_dequant_drops_scale": ("orc_e4m3_value(codes[r * dim + d]) * (double)scales[r];",
                                 "orc_e4m3_value(codes[r * dim + d]);"),
+    "int4_scale_over_8": ("float step = amax / 7.0f;", "float step = amax / 8.0f;"),
+    "int4_truncates": ("q = nearbyintf((float)elem(dtype, rows, r * dim + 2 * j + half) / step);",
+                       "q = truncf((float)elem(dtype, rows, r * dim + 2 * j + half) / step);"),
+    "int4_nibbles_swapped": ("(uint8_t)(u[0] | (u[1] << 4));", "(uint8_t)(u[1] | (u[0] << 4));"),
+    "int4_twos_complement_codes": ("u[half] = (int)q + 8;", "u[half] = (int)q & 15;"),
+    "int4_dequant_nibble_order": ("int u = (d % 2) ? (byte >> 4) : (byte & 15);",
+                                  "int u = (d % 2) ? (byte & 15) : (byte >> 4);"),
+    "int4_dequant_no_offset": ("out[r * dim + d] = (double)(u - 8) * (double)scales[r];",
+                               "out[r * dim + d] = (double)u * (double)scales[r];"),
+    "int4_store_scale_at_offset": ("value_cache + crow * row_bytes, value_scale + crow);",
+                                   "value_cache + crow * row_bytes, value_scale + pos);"),
 }
 
 
