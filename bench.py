@@ -54,15 +54,26 @@ def decode_bytes_q8(c) -> int:
                + 4 * nb.sum() + 4 * c.num_seqs)
 
 
+def decode_bytes_q4(c) -> int:
+    """Algorithmic bytes of one decode call over an int4 cache: the half-byte codes of K and V of every
+    context token, their fp32 row scales, q and out (bf16), the block-table entries used and context_lens."""
+    lens = c.context_lens.astype(np.int64)
+    nb = -(-lens // c.block_size)
+    return int(2 * lens.sum() * c.num_kv_heads * (c.head_dim // 2 + 4) + 2 * c.num_seqs * c.num_heads * c.head_dim * 2
+               + 4 * nb.sum() + 4 * c.num_seqs)
+
+
 Q8_LEGS = {
     "int8": ("int8 codes + fp32 scale per (token, kv head) row", "kv_cache_store_int8", "paged_attention_decode_int8"),
     "fp8": ("float8 E4M3 codes + fp32 scale per (token, kv head) row", "kv_cache_store_fp8",
             "paged_attention_decode_fp8"),
+    "int4": ("int4 codes (two per byte) + fp32 scale per (token, kv head) row", "kv_cache_store_int4",
+             "paged_attention_decode_int4"),
 }
 
 
 def bench_q8(kind, pkv, torch, W, c, dev, copies, steps, warmup):
-    """The same decode workload over an 8-bit cache (rows quantized by the library's store from the bf16
+    """The same decode workload over a quantized cache (rows quantized by the library's store from the bf16
     values; pool copies rotated as in the main leg): average decode-call time from HIP events."""
     what, store_name, decode_name = Q8_LEGS[kind]
     store, decode = getattr(pkv, store_name), getattr(pkv, decode_name)
@@ -72,7 +83,7 @@ def bench_q8(kind, pkv, torch, W, c, dev, copies, steps, warmup):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
     kr, vr, slots = tt(kr), tt(vr), torch.from_numpy(slots).to(dev)
-    shape = (c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
+    shape = (c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim // 2 if kind == "int4" else c.head_dim)
     pools = []
     for _ in range(copies):
         kc = torch.zeros(shape, dtype=torch.int8 if kind == "int8" else torch.uint8, device=dev)
@@ -99,7 +110,7 @@ def bench_q8(kind, pkv, torch, W, c, dev, copies, steps, warmup):
             ev[k - warmup][1].record(stream)
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    nbytes = decode_bytes_q8(c)
+    nbytes = decode_bytes_q4(c) if kind == "int4" else decode_bytes_q8(c)
     return {"workload": c.name, "cache": what,
             "decode_ms": round(ms, 5), "algorithmic_bytes": nbytes,
             "achieved_gbs": round(nbytes / (ms * 1e-3) / 1e9, 2),
@@ -280,7 +291,7 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="pool copies rotated per step (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
-    ap.add_argument("--no-int8", action="store_true", help="skip the 8-bit-cache (int8, fp8) decode legs")
+    ap.add_argument("--no-int8", action="store_true", help="skip the quantized-cache (int8, fp8, int4) decode legs")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -439,7 +450,7 @@ def main():
     }
     if c.dtype == "bf16" and c.head_dim == 128 and c.block_size >= 16 and not args.no_int8:
         pools = None
-        for kind in ("int8", "fp8"):
+        for kind in ("int8", "fp8", "int4"):
             leg = bench_q8(kind, pkv, torch, W, c, dev, copies, args.steps, args.warmup)
             leg["speedup_vs_bf16_cache"] = round(dec_avg_ms / leg["decode_ms"], 3)
             result[f"{kind}_cache"] = leg

@@ -12,7 +12,9 @@
  *                               the same over an int8 cache;
  *   pkv_kv_cache_store_fp8, pkv_paged_attention_decode_fp8, pkv_paged_attention_prefill_fp8:
  *                               the same over an fp8 (E4M3) cache;
- *   pkv_paged_attention_decode_plan and pkv_paged_attention_decode_run (_int8_run, _fp8_run):
+ *   pkv_kv_cache_store_int4, pkv_paged_attention_decode_int4:
+ *                               store and decode over an int4 cache (two codes per byte);
+ *   pkv_paged_attention_decode_plan and pkv_paged_attention_decode_run (_int8_run, _fp8_run, _int4_run):
  *                               a decode call in two halves, the work list built once per step
  *                               and reused by every layer's attention.
  *
@@ -63,7 +65,7 @@ extern "C" {
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
 /* The cache a decode plan is made for: elements of the query's dtype, int8 codes or E4M3 codes. */
-typedef enum { PKV_CACHE_ELEMENTS = 0, PKV_CACHE_INT8 = 1, PKV_CACHE_FP8 = 2 } pkv_cache_kind;
+typedef enum { PKV_CACHE_ELEMENTS = 0, PKV_CACHE_INT8 = 1, PKV_CACHE_FP8 = 2, PKV_CACHE_INT4 = 3 } pkv_cache_kind;
 
 typedef enum {
     PKV_OK = 0,
@@ -269,18 +271,55 @@ pkv_status pkv_paged_attention_prefill_fp8(pkv_dtype dtype, void *out, const voi
                                            int32_t causal, hipStream_t stream);
 
 /*
+ * int4 KV cache (same passage, which names int4 beside int8). The pages fix no scheme; this library keeps
+ * one fp32 scale per (token, kv head) row and two 4-bit codes per byte:
+ *   scale = max_d |x_d| / 7,  q_d = round_half_even(x_d / scale) clamped to [-7, 7],  u_d = q_d + 8,
+ * computed in fp32 with IEEE division (a row of zeros: scale 0, u = 8); element 2j in the low four bits of
+ * byte j, element 2j + 1 in the high four bits. Dequantized, x_d ~ q_d * scale with |error| <= scale / 2.
+ *   key_cache, value_cache  uint8 [num_blocks][num_kv_heads][block_size][head_dim / 2];
+ *   key_scale, value_scale  fp32 [num_blocks][num_kv_heads][block_size], one per cache row.
+ */
+
+/*
+ * kv_cache_store_int4: pkv_kv_cache_store_int8 with the int4 codes above (rows of head_dim / 2 bytes).
+ * key / value PKV_F32 or PKV_BF16, head_dim 64 or 128; rows must be finite. Cache pointers 16-byte aligned,
+ * scales 4-byte aligned.
+ */
+pkv_status pkv_kv_cache_store_int4(pkv_dtype dtype, const void *key, const void *value, uint8_t *key_cache,
+                                   uint8_t *value_cache, float *key_scale, float *value_scale,
+                                   const int32_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int64_t num_blocks, hipStream_t stream);
+
+/*
+ * paged_attention_decode_int4: pkv_paged_attention_decode over an int4 cache: attention over the
+ * dequantized K/V ((u - 8) * scale). dtype (query and out) must be PKV_BF16, head_dim 128, block_size >= 16
+ * (PKV_EUNSUPPORTED otherwise). The codes enter the MFMA products as the exact bf16 values 136 + q; the
+ * scores subtract 136 times the head's query sum, the outputs 136 times the sum of the bf16 weights that
+ * multiplied V (fp32). Otherwise as pkv_paged_attention_decode_int8: K scale times each score, V scale
+ * times each weight before its bf16 rounding, denominator over the unrounded weights. Scale arrays 16-byte
+ * aligned. Workspace: pkv_paged_attention_decode_workspace_size with the same sizes.
+ */
+pkv_status pkv_paged_attention_decode_int4(pkv_dtype dtype, void *out, const void *query, const uint8_t *key_cache,
+                                           const uint8_t *value_cache, const float *key_scale,
+                                           const float *value_scale, const int32_t *block_tables,
+                                           int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
+                                           int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * paged_attention_decode_plan / paged_attention_decode_run: one decode call in two halves. A model runs
  * the same attention metadata (context_lens, block_tables) through every layer of a step (nano-vllm
  * walkthrough, section 2 context: the context is set once per forward pass and read by each layer's
  * attention), so the work list that pkv_paged_attention_decode builds from context_lens on every call can
  * be built once: pkv_paged_attention_decode_plan writes it into `workspace`; each
- * pkv_paged_attention_decode_run (or _int8_run / _fp8_run over an 8-bit cache) then decodes from it and
+ * pkv_paged_attention_decode_run (or _int8_run / _fp8_run / _int4_run over a quantized cache) then decodes from it and
  * writes out, exactly as the whole call would (bit-identical results).
  * plan: context_lens (device int32 [num_seqs]) and the sizes a run will use; cache_kind is the cache the runs
- *   read (PKV_CACHE_ELEMENTS: the query's dtype; PKV_CACHE_INT8 / _FP8: an 8-bit cache, which needs a
- *   bf16 query, head_dim 128 and block_size >= 16), which sizes the parts for that kernel. Errors as for
+ *   read (PKV_CACHE_ELEMENTS: the query's dtype; PKV_CACHE_INT8 / _FP8 / _INT4: a quantized cache, which
+ *   needs a bf16 query, head_dim 128 and block_size >= 16), which sizes the parts for that kernel. Errors as for
  *   pkv_paged_attention_decode (no cache or output pointers are taken).
- * run: the arguments of pkv_paged_attention_decode (or of its _int8 / _fp8 form) without context_lens. It
+ * run: the arguments of pkv_paged_attention_decode (or of its _int8 / _fp8 / _int4 form) without context_lens. It
  *   needs a workspace planned with the same num_seqs, max_context_len, num_heads, num_kv_heads, head_dim,
  *   block_size and context_lens (the caller's contract: the work list records token ranges; a run over a
  *   stale plan attends over the planned lengths), and reads the plan in stream order. A whole decode call
@@ -314,6 +353,14 @@ pkv_status pkv_paged_attention_decode_fp8_run(pkv_dtype dtype, void *out, const 
                                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                               int64_t num_blocks, float scale, void *workspace,
                                               size_t workspace_bytes, hipStream_t stream);
+pkv_status pkv_paged_attention_decode_int4_run(pkv_dtype dtype, void *out, const void *query,
+                                               const uint8_t *key_cache, const uint8_t *value_cache,
+                                               const float *key_scale, const float *value_scale,
+                                               const int32_t *block_tables, int32_t block_table_stride,
+                                               int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                               int64_t num_blocks, float scale, void *workspace,
+                                               size_t workspace_bytes, hipStream_t stream);
 
 /* Message of the calling thread's last non-OK status ("" if none). Owned by the library. */
 const char *pkv_last_error(void);

@@ -60,6 +60,11 @@ def load_library(path: str = LIB_PATH):
                                                 I64, F, P, SZ, P],
         "pkv_paged_attention_decode_fp8_run": [ctypes.c_int, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
                                                I64, F, P, SZ, P],
+        "pkv_kv_cache_store_int4": [ctypes.c_int, P, P, P, P, P, P, P, I64, I32, I32, I32, I64, P],
+        "pkv_paged_attention_decode_int4": [ctypes.c_int, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32,
+                                            I64, F, P, SZ, P],
+        "pkv_paged_attention_decode_int4_run": [ctypes.c_int, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
+                                                I64, F, P, SZ, P],
         "pkv_paged_attention_prefill_int8": [ctypes.c_int, P, P, P, P, P, P, P, I32, P, P, I32, I32, I32, I32, I32,
                                              I32, I32, I64, F, I32, P],
         "pkv_paged_attention_prefill_fp8": [ctypes.c_int, P, P, P, P, P, P, P, I32, P, P, I32, I32, I32, I32, I32,
@@ -207,7 +212,7 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
                                           _ptr(workspace), ws_bytes, _stream(stream)))
 
 
-_CACHE_KINDS = {"elements": 0, "int8": 1, "fp8": 2}
+_CACHE_KINDS = {"elements": 0, "int8": 1, "fp8": 2, "int4": 3}
 
 
 def paged_attention_decode_plan(context_lens, max_context_len, num_heads, num_kv_heads, head_dim, block_size,
@@ -251,17 +256,23 @@ def paged_attention_decode_run(out, query, key_cache, value_cache, block_tables,
                                               ws_bytes, _stream(stream)))
 
 
-_CODE_DTYPES = {"int8": (torch.int8,), "fp8": (torch.uint8, torch.float8_e4m3fn)}
+_CODE_DTYPES = {"int8": (torch.int8,), "fp8": (torch.uint8, torch.float8_e4m3fn), "int4": (torch.uint8,)}
+
+
+def _cache_dims(kind, key_cache):
+    """(NB, Hkv, bs, head_dim) of a quantized cache: int4 rows hold two codes per byte."""
+    nb, hkv, bs, last = key_cache.shape
+    return nb, hkv, bs, 2 * last if kind == "int4" else last
 
 
 def _store_q8(kind, key, value, key_cache, value_cache, key_scale, value_scale, slot_mapping, stream):
     lib = load_library()
     _dev(key, value, key_cache, value_cache, key_scale, value_scale, slot_mapping)
     _i32(slot_mapping)
-    nb, hkv, bs, d = key_cache.shape
+    nb, hkv, bs, d = _cache_dims(kind, key_cache)
     n = key.shape[0]
     if key.shape != (n, hkv, d) or value.shape != key.shape or value_cache.shape != key_cache.shape:
-        raise ValueError("key/value must be [N, Hkv, D] and both caches [NB, Hkv, bs, D]")
+        raise ValueError("key/value must be [N, Hkv, D] and both caches [NB, Hkv, bs, D] (D / 2 bytes for int4)")
     if key_scale.shape != (nb, hkv, bs) or value_scale.shape != (nb, hkv, bs):
         raise ValueError("scales must be [NB, Hkv, bs]")
     if key_cache.dtype not in _CODE_DTYPES[kind] or value_cache.dtype not in _CODE_DTYPES[kind]:
@@ -270,7 +281,8 @@ def _store_q8(kind, key, value, key_cache, value_cache, key_scale, value_scale, 
         raise ValueError("float32 scales expected")
     if slot_mapping.shape != (n,) or key.dtype != value.dtype:
         raise ValueError("slot_mapping must have one entry per token; key and value share a dtype")
-    fn = lib.pkv_kv_cache_store_int8 if kind == "int8" else lib.pkv_kv_cache_store_fp8
+    fn = {"int8": lib.pkv_kv_cache_store_int8, "fp8": lib.pkv_kv_cache_store_fp8,
+          "int4": lib.pkv_kv_cache_store_int4}[kind]
     _check(fn(_dtype_code(key), _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(key_scale),
               _ptr(value_scale), _ptr(slot_mapping), n, hkv, d, bs, nb, _stream(stream)))
 
@@ -280,7 +292,7 @@ def _decode_q8(kind, out, query, key_cache, value_cache, key_scale, value_scale,
     lib = load_library()
     _dev(out, query, key_cache, value_cache, key_scale, value_scale, block_tables, context_lens, workspace)
     _i32(block_tables, context_lens)
-    nb, hkv, bs, d = key_cache.shape
+    nb, hkv, bs, d = _cache_dims(kind, key_cache)
     b, hq, d2 = query.shape
     if d2 != d or out.shape != query.shape or value_cache.shape != key_cache.shape:
         raise ValueError("query/out must be [B, Hq, D] with the caches' D")
@@ -295,7 +307,8 @@ def _decode_q8(kind, out, query, key_cache, value_cache, key_scale, value_scale,
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=query.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    fn = lib.pkv_paged_attention_decode_int8 if kind == "int8" else lib.pkv_paged_attention_decode_fp8
+    fn = {"int8": lib.pkv_paged_attention_decode_int8, "fp8": lib.pkv_paged_attention_decode_fp8,
+          "int4": lib.pkv_paged_attention_decode_int4}[kind]
     _check(fn(_dtype_code(query), _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(key_scale),
               _ptr(value_scale), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), b,
               int(max_context_len), hq, hkv, d, bs, nb, float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
@@ -306,7 +319,7 @@ def _decode_q8_run(kind, out, query, key_cache, value_cache, key_scale, value_sc
     lib = load_library()
     _dev(out, query, key_cache, value_cache, key_scale, value_scale, block_tables, workspace)
     _i32(block_tables)
-    nb, hkv, bs, d = key_cache.shape
+    nb, hkv, bs, d = _cache_dims(kind, key_cache)
     b, hq, d2 = query.shape
     if d2 != d or out.shape != query.shape or value_cache.shape != key_cache.shape:
         raise ValueError("query/out must be [B, Hq, D] with the caches' D")
@@ -318,7 +331,8 @@ def _decode_q8_run(kind, out, query, key_cache, value_cache, key_scale, value_sc
     if block_tables.dim() != 2 or block_tables.shape[0] != b:
         raise ValueError("block_tables must be [B, stride]")
     ws_bytes = workspace.numel() * workspace.element_size()
-    fn = lib.pkv_paged_attention_decode_int8_run if kind == "int8" else lib.pkv_paged_attention_decode_fp8_run
+    fn = {"int8": lib.pkv_paged_attention_decode_int8_run, "fp8": lib.pkv_paged_attention_decode_fp8_run,
+          "int4": lib.pkv_paged_attention_decode_int4_run}[kind]
     _check(fn(_dtype_code(query), _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(key_scale),
               _ptr(value_scale), _ptr(block_tables), block_tables.shape[1], b, int(max_context_len), hq, hkv, d, bs,
               nb, float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
@@ -364,6 +378,28 @@ def paged_attention_decode_fp8(out, query, key_cache, value_cache, key_scale, va
     """Decode attention over an fp8 (E4M3) cache; otherwise as ``paged_attention_decode_int8``."""
     _decode_q8("fp8", out, query, key_cache, value_cache, key_scale, value_scale, block_tables, context_lens,
                max_context_len, scale, workspace, stream)
+
+
+def kv_cache_store_int4(key, value, key_cache, value_cache, key_scale, value_scale, slot_mapping, stream=None):
+    """``kv_cache_store_int8`` with 4-bit codes: scale max|x| / 7, q = round-half-even(x / scale) in [-7, 7],
+    stored as q + 8, two per byte (element 2j in the low four bits of byte j); the caches are uint8
+    [NB, Hkv, bs, D / 2]."""
+    _store_q8("int4", key, value, key_cache, value_cache, key_scale, value_scale, slot_mapping, stream)
+
+
+def paged_attention_decode_int4(out, query, key_cache, value_cache, key_scale, value_scale, block_tables,
+                                context_lens, max_context_len, scale, workspace=None, stream=None):
+    """Decode attention over an int4 cache (uint8 [NB, Hkv, bs, D / 2], fp32 scales [NB, Hkv, bs]); otherwise as
+    ``paged_attention_decode_int8``."""
+    _decode_q8("int4", out, query, key_cache, value_cache, key_scale, value_scale, block_tables, context_lens,
+               max_context_len, scale, workspace, stream)
+
+
+def paged_attention_decode_int4_run(out, query, key_cache, value_cache, key_scale, value_scale, block_tables,
+                                    max_context_len, scale, workspace, stream=None):
+    """``paged_attention_decode_int4`` from a work list made by ``paged_attention_decode_plan(cache="int4")``."""
+    _decode_q8_run("int4", out, query, key_cache, value_cache, key_scale, value_scale, block_tables,
+                   max_context_len, scale, workspace, stream)
 
 
 def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, cu_seqlens_q, cu_seqlens_k,

@@ -296,9 +296,10 @@ pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *qu
 
 namespace {
 
-// Shared bodies of the int8 and fp8 entry points (the same layouts, checks and kernels; only the code type
-// differs).
-pkv_status store_q8(bool fp8, const char *what, pkv_dtype dtype, const void *key, const void *value,
+// Shared bodies of the int8, fp8 and int4 entry points (the same layouts up to the row bytes, checks and
+// kernels; only the code type differs). format: 0 int8, 1 fp8, 2 int4.
+enum { Q_INT8 = 0, Q_FP8 = 1, Q_INT4 = 2 };
+pkv_status store_q8(int format, const char *what, pkv_dtype dtype, const void *key, const void *value,
                     void *key_cache, void *value_cache, float *key_scale, float *value_scale,
                     const int32_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
                     int32_t block_size, int64_t num_blocks, hipStream_t stream) {
@@ -312,21 +313,23 @@ pkv_status store_q8(bool fp8, const char *what, pkv_dtype dtype, const void *key
                 ((uintptr_t)key_scale & 3u) == 0 && ((uintptr_t)value_scale & 3u) == 0,
             PKV_EINVAL, "key, value and cache pointers must be 16-byte aligned, scales 4-byte aligned");
     REQUIRE(num_tokens * num_kv_heads <= (int64_t)1 << 40, PKV_EINVAL, "num_tokens too large");
-    return hip_status(pkv::launch_store_q8(dtype == PKV_BF16, fp8, head_dim, key, value, key_cache, value_cache,
+    return hip_status(pkv::launch_store_q8(dtype == PKV_BF16, format, head_dim, key, value, key_cache, value_cache,
                                            key_scale, value_scale, slot_mapping, num_tokens, num_kv_heads, block_size,
                                            (int)num_blocks, stream),
                       what);
 }
 
-pkv_status decode_q8(bool fp8, const char *what, pkv_dtype dtype, void *out, const void *query,
+pkv_status decode_q8(int format, const char *what, pkv_dtype dtype, void *out, const void *query,
                      const void *key_cache, const void *value_cache, const float *key_scale,
                      const float *value_scale, const int32_t *block_tables, int32_t block_table_stride,
                      const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
                      void *workspace, size_t workspace_bytes, hipStream_t stream, DecodeMode mode = DECODE_CALL) {
-    REQUIRE(dtype == PKV_BF16, PKV_EUNSUPPORTED, "8-bit-cache decode takes a bf16 query (got dtype %d)", (int)dtype);
-    REQUIRE(head_dim == 128, PKV_EUNSUPPORTED, "8-bit-cache decode supports head_dim 128 (got %d)", head_dim);
-    REQUIRE(block_size >= 16, PKV_EUNSUPPORTED, "8-bit-cache decode needs block_size >= 16 (got %d)", block_size);
+    REQUIRE(dtype == PKV_BF16, PKV_EUNSUPPORTED, "quantized-cache decode takes a bf16 query (got dtype %d)",
+            (int)dtype);
+    REQUIRE(head_dim == 128, PKV_EUNSUPPORTED, "quantized-cache decode supports head_dim 128 (got %d)", head_dim);
+    REQUIRE(block_size >= 16, PKV_EUNSUPPORTED, "quantized-cache decode needs block_size >= 16 (got %d)",
+            block_size);
     pkv::DecodeArgs a{};
     pkv_status st = decode_args(a, dtype, out, query, key_cache, value_cache, block_tables, block_table_stride,
                                 context_lens, num_seqs, max_context_len, num_heads, num_kv_heads, head_dim, block_size,
@@ -337,7 +340,8 @@ pkv_status decode_q8(bool fp8, const char *what, pkv_dtype dtype, void *out, con
             "scale arrays must be 16-byte aligned");
     a.key_scale = key_scale;
     a.value_scale = value_scale;
-    a.fp8_codes = fp8;
+    a.fp8_codes = format == Q_FP8;
+    a.int4_codes = format == Q_INT4;
     return hip_status(pkv::launch_decode_q8(a, num_heads / num_kv_heads, stream), what);
 }
 
@@ -349,7 +353,7 @@ pkv_status pkv_kv_cache_store_int8(pkv_dtype dtype, const void *key, const void 
                                    int8_t *value_cache, float *key_scale, float *value_scale,
                                    const int32_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                                    int32_t head_dim, int32_t block_size, int64_t num_blocks, hipStream_t stream) {
-    return store_q8(false, "kv_cache_store_int8 launch", dtype, key, value, key_cache, value_cache, key_scale,
+    return store_q8(Q_INT8, "kv_cache_store_int8 launch", dtype, key, value, key_cache, value_cache, key_scale,
                     value_scale, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size, num_blocks, stream);
 }
 
@@ -360,7 +364,7 @@ pkv_status pkv_paged_attention_decode_int8(pkv_dtype dtype, void *out, const voi
                                            int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
                                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    return decode_q8(false, "paged_attention_decode_int8 launch", dtype, out, query, key_cache, value_cache,
+    return decode_q8(Q_INT8, "paged_attention_decode_int8 launch", dtype, out, query, key_cache, value_cache,
                      key_scale, value_scale, block_tables, block_table_stride, context_lens, num_seqs,
                      max_context_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace,
                      workspace_bytes, stream);
@@ -370,7 +374,7 @@ pkv_status pkv_kv_cache_store_fp8(pkv_dtype dtype, const void *key, const void *
                                   uint8_t *value_cache, float *key_scale, float *value_scale,
                                   const int32_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t block_size, int64_t num_blocks, hipStream_t stream) {
-    return store_q8(true, "kv_cache_store_fp8 launch", dtype, key, value, key_cache, value_cache, key_scale,
+    return store_q8(Q_FP8, "kv_cache_store_fp8 launch", dtype, key, value, key_cache, value_cache, key_scale,
                     value_scale, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size, num_blocks, stream);
 }
 
@@ -381,7 +385,28 @@ pkv_status pkv_paged_attention_decode_fp8(pkv_dtype dtype, void *out, const void
                                           int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
                                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
                                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    return decode_q8(true, "paged_attention_decode_fp8 launch", dtype, out, query, key_cache, value_cache,
+    return decode_q8(Q_FP8, "paged_attention_decode_fp8 launch", dtype, out, query, key_cache, value_cache,
+                     key_scale, value_scale, block_tables, block_table_stride, context_lens, num_seqs,
+                     max_context_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace,
+                     workspace_bytes, stream);
+}
+
+pkv_status pkv_kv_cache_store_int4(pkv_dtype dtype, const void *key, const void *value, uint8_t *key_cache,
+                                   uint8_t *value_cache, float *key_scale, float *value_scale,
+                                   const int32_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int64_t num_blocks, hipStream_t stream) {
+    return store_q8(Q_INT4, "kv_cache_store_int4 launch", dtype, key, value, key_cache, value_cache, key_scale,
+                    value_scale, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size, num_blocks, stream);
+}
+
+pkv_status pkv_paged_attention_decode_int4(pkv_dtype dtype, void *out, const void *query, const uint8_t *key_cache,
+                                           const uint8_t *value_cache, const float *key_scale,
+                                           const float *value_scale, const int32_t *block_tables,
+                                           int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
+                                           int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return decode_q8(Q_INT4, "paged_attention_decode_int4 launch", dtype, out, query, key_cache, value_cache,
                      key_scale, value_scale, block_tables, block_table_stride, context_lens, num_seqs,
                      max_context_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace,
                      workspace_bytes, stream);
@@ -391,14 +416,17 @@ pkv_status pkv_paged_attention_decode_plan(pkv_dtype dtype, int32_t cache_kind, 
                                            int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
                                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    REQUIRE(cache_kind == PKV_CACHE_ELEMENTS || cache_kind == PKV_CACHE_INT8 || cache_kind == PKV_CACHE_FP8,
-            PKV_EINVAL, "cache_kind %d is not PKV_CACHE_ELEMENTS, _INT8 or _FP8", cache_kind);
+    REQUIRE(cache_kind == PKV_CACHE_ELEMENTS || cache_kind == PKV_CACHE_INT8 || cache_kind == PKV_CACHE_FP8 ||
+                cache_kind == PKV_CACHE_INT4,
+            PKV_EINVAL, "cache_kind %d is not PKV_CACHE_ELEMENTS, _INT8, _FP8 or _INT4", cache_kind);
     const bool q8 = cache_kind != PKV_CACHE_ELEMENTS;
     if (q8) {
-        REQUIRE(dtype == PKV_BF16, PKV_EUNSUPPORTED, "8-bit-cache decode takes a bf16 query (got dtype %d)",
+        REQUIRE(dtype == PKV_BF16, PKV_EUNSUPPORTED, "quantized-cache decode takes a bf16 query (got dtype %d)",
                 (int)dtype);
-        REQUIRE(head_dim == 128, PKV_EUNSUPPORTED, "8-bit-cache decode supports head_dim 128 (got %d)", head_dim);
-        REQUIRE(block_size >= 16, PKV_EUNSUPPORTED, "8-bit-cache decode needs block_size >= 16 (got %d)", block_size);
+        REQUIRE(head_dim == 128, PKV_EUNSUPPORTED, "quantized-cache decode supports head_dim 128 (got %d)",
+                head_dim);
+        REQUIRE(block_size >= 16, PKV_EUNSUPPORTED, "quantized-cache decode needs block_size >= 16 (got %d)",
+                block_size);
     }
     pkv::DecodeArgs a{};
     const pkv_status st = decode_args(a, dtype, nullptr, nullptr, nullptr, nullptr, nullptr,
@@ -433,7 +461,7 @@ pkv_status pkv_paged_attention_decode_int8_run(pkv_dtype dtype, void *out, const
                                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                                int64_t num_blocks, float scale, void *workspace,
                                                size_t workspace_bytes, hipStream_t stream) {
-    return decode_q8(false, "paged_attention_decode_int8_run launch", dtype, out, query, key_cache, value_cache,
+    return decode_q8(Q_INT8, "paged_attention_decode_int8_run launch", dtype, out, query, key_cache, value_cache,
                      key_scale, value_scale, block_tables, block_table_stride, nullptr, num_seqs, max_context_len,
                      num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace, workspace_bytes,
                      stream, DECODE_RUN_ONLY);
@@ -447,7 +475,21 @@ pkv_status pkv_paged_attention_decode_fp8_run(pkv_dtype dtype, void *out, const 
                                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                               int64_t num_blocks, float scale, void *workspace,
                                               size_t workspace_bytes, hipStream_t stream) {
-    return decode_q8(true, "paged_attention_decode_fp8_run launch", dtype, out, query, key_cache, value_cache,
+    return decode_q8(Q_FP8, "paged_attention_decode_fp8_run launch", dtype, out, query, key_cache, value_cache,
+                     key_scale, value_scale, block_tables, block_table_stride, nullptr, num_seqs, max_context_len,
+                     num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace, workspace_bytes,
+                     stream, DECODE_RUN_ONLY);
+}
+
+pkv_status pkv_paged_attention_decode_int4_run(pkv_dtype dtype, void *out, const void *query,
+                                               const uint8_t *key_cache, const uint8_t *value_cache,
+                                               const float *key_scale, const float *value_scale,
+                                               const int32_t *block_tables, int32_t block_table_stride,
+                                               int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                               int64_t num_blocks, float scale, void *workspace,
+                                               size_t workspace_bytes, hipStream_t stream) {
+    return decode_q8(Q_INT4, "paged_attention_decode_int4_run launch", dtype, out, query, key_cache, value_cache,
                      key_scale, value_scale, block_tables, block_table_stride, nullptr, num_seqs, max_context_len,
                      num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace, workspace_bytes,
                      stream, DECODE_RUN_ONLY);

@@ -564,19 +564,40 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byt
 __device__ __forceinline__ u32x2 buffer_load8(__amdgpu_buffer_rsrc_t r, int byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, PKV_DECODE_NT ? 2 : 0);
 }
+__device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, PKV_DECODE_NT ? 2 : 0);
+}
 
-// Registers of one 32-token tile of the matrix-core decode: bf16 rows, or int8 codes plus per-row scales.
-template <bool Q8>
+// Four-bit codes u (element e of a 32-bit word in bits 4 e .. 4 e + 3) to bf16 pairs without conversion
+// instructions: 0x4300 | u is the bf16 of 128 + u (the exponent of 128 puts the mantissa's last bit at 1),
+// so pair k = ((w >> 4 k) & 0x000f000f) | 0x43004300 holds elements k and k + 4 as 128 + u. With u = q + 8
+// the values are 136 + q; the decode subtracts 136 times the matching sums (I4_BIAS).
+constexpr float I4_BIAS = 136.0f;
+template <int K>
+__device__ __forceinline__ uint32_t nibble_pair_to_bf16x2(uint32_t w) {
+    return ((w >> (4 * K)) & 0x000f000fu) | 0x43004300u;
+}
+
+// Registers of one 32-token tile of the matrix-core decode: bf16 rows, or 8-bit codes plus per-row scales,
+// or 4-bit codes plus per-row scales.
+template <bool Q8, bool I4 = false>
 struct MfmaTile {
     u32x4 k[2][4];
     u32x4 v[2][4];
     bool live[2];                           // group's block id lies in the pool
 };
 template <>
-struct MfmaTile<true> {
+struct MfmaTile<true, false> {
     u32x4 k[2][2];                          // per group: dims 16 b .. +16 and 64 + 16 b .. +16 of row n
     u32x2 v[2][4];                          // per group and i: dims 8 n .. +8 of row 4 b + i
     f32x4 ks[2], vs[2];                     // scales of rows 4 b .. 4 b + 3 of each group
+    bool live[2];
+};
+template <>
+struct MfmaTile<true, true> {
+    u32x4 k[2];                             // per group: dims 32 b .. 32 b + 32 of row n (word c: 32 b + 8 c ..)
+    uint32_t v[2][4];                       // per group and i: dims 8 n .. +8 of row 4 b + i
+    f32x4 ks[2], vs[2];
     bool live[2];
 };
 
@@ -627,7 +648,7 @@ constexpr int DECODE_CU_WAVES_Q8 = 8;
 #endif
 constexpr int DECODE_CLAIM_LEAD = PKV_DECODE_CLAIM_LEAD;  // tiles left in a unit when the next is claimed
 
-template <int G, bool Q8, bool F8, int NWV = Q8 ? DECODE_CU_WAVES_Q8 : DECODE_CU_WAVES_BF16>
+template <int G, bool Q8, bool F8, bool I4 = false, int NWV = Q8 ? DECODE_CU_WAVES_Q8 : DECODE_CU_WAVES_BF16>
 __global__ void __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const char *__restrict__ key_cache,
                    const char *__restrict__ value_cache, const int32_t *__restrict__ block_tables, int bt_stride,
@@ -637,8 +658,10 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
                    const float *__restrict__ key_scale, const float *__restrict__ value_scale) {
     static_assert(G >= 1 && G <= 16, "query heads per kv head");
     constexpr int D = 128, CH = D / 8;        // 16-byte chunks of a bf16 row
-    constexpr int RB = Q8 ? D : 2 * D;        // bytes per cache row
+    static_assert(!I4 || (Q8 && !F8), "4-bit codes use the quantized-cache path");
+    constexpr int RB = I4 ? D / 2 : Q8 ? D : 2 * D;     // bytes per cache row
     constexpr int TILE = 32;
+    constexpr uint32_t ONES = 0x3f803f80u;    // bf16 pair (1, 1)
     const int lane = threadIdx.x & 63, n = lane & 15, b = lane >> 4;
     const int num_heads = num_kv_heads * G;
     const int bs_mask = (1 << log2_bs) - 1;
@@ -697,12 +720,12 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
         const int64_t row = ((int64_t)x.seq * num_heads + x.kvh * G + (n < G ? n : 0)) * CH;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const int chunk = Q8 ? (c < 2 ? 2 * b + c : 8 + 2 * b + (c - 2)) : 4 * c + b;
+            const int chunk = I4 ? 4 * b + c : Q8 ? (c < 2 ? 2 * b + c : 8 + 2 * b + (c - 2)) : 4 * c + b;
             dst[c] = n < G ? qv[row + chunk] : u32x4{0, 0, 0, 0};
         }
     };
 
-    using Tile = MfmaTile<Q8>;
+    using Tile = MfmaTile<Q8, I4>;
     // Rows past the unit's end are clamped to its last token (same block: a group past the end is
     // clamped whole), so every lane reads a row holding finite data; such tokens get zero weight.
     // Loads go through buffer descriptors of the group's (block, kv head) slab: wave-uniform base,
@@ -723,12 +746,18 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
                 (void *)(value_cache + slab * RB), (short)0, (int)slab_bytes, BUF_RSRC_W3);
             const int last = x.ntok - 1 - tl0;              // rows past it are clamped to it
             const int r0 = (tokc & bs_mask) - tlc + tl0;    // slab row of token tl0
-            if constexpr (Q8) {
+            if constexpr (I4) {
+                t.k[g] = buffer_load16(kr, (r0 + min(n, last)) * RB + 16 * b);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t.v[g][i] = buffer_load4(vr, (r0 + min(4 * b + i, last)) * RB + 4 * n);
+            } else if constexpr (Q8) {
                 const int koff = (r0 + min(n, last)) * RB + 16 * b;
                 t.k[g][0] = buffer_load16(kr, koff);
                 t.k[g][1] = buffer_load16(kr, koff + 64);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) t.v[g][i] = buffer_load8(vr, (r0 + min(4 * b + i, last)) * RB + 8 * n);
+            }
+            if constexpr (Q8) {
                 // scales of the 16-row group holding the clamped token (its own rows when the group is live)
                 const int srow = (tokc & bs_mask) & ~15;
                 const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
@@ -751,8 +780,29 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
     f32x4 acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // 4-bit codes enter the products as 136 + q (nibble_pair_to_bf16x2). Scores then carry 136 times the
+    // head's query sum (kcorr, subtracted from every score), and the accumulators 136 times the sum of the
+    // bf16 weights they took (vsum, kept beside l and subtracted in finish). The K operand pairs elements
+    // k and k + 4 of each 8-element chunk, so the query chunk is reordered to match when the unit starts.
+    float kcorr = 0.f, vsum = 0.f;
+    auto prep_q = [&]() {
+        float qs = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 w = qt[c];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qs = dot2_bf16(w[e], ONES, qs);
+            qt[c] = u32x4{pair_lo(w[0], w[2]), pair_hi(w[0], w[2]), pair_lo(w[1], w[3]), pair_hi(w[1], w[3])};
+        }
+        qs += __shfl_xor(qs, 16);
+        qs += __shfl_xor(qs, 32);
+        kcorr = I4_BIAS * qs;
+    };
 
     auto compute = [&](const Unit &x, int tile, Tile &t) {
+        if constexpr (I4) {
+            if (tile == 0) prep_q();                // the unit's queries arrived with (or before) its first tile
+        }
         // masked tokens: past the unit's end (only in its last tile), or in a block outside the pool,
         // whose rows (block 0) may hold anything: those get V zeroed as well
         const bool partial = (tile + 1) * TILE > x.ntok || !t.live[0] || !t.live[1];   // wave-uniform
@@ -760,7 +810,20 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
         u32x4 tk[2][4], tv[2][4];
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-            if constexpr (Q8) {
+            if constexpr (I4) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t w = t.k[g][c];
+                    tk[g][c] = u32x4{nibble_pair_to_bf16x2<0>(w), nibble_pair_to_bf16x2<1>(w),
+                                     nibble_pair_to_bf16x2<2>(w), nibble_pair_to_bf16x2<3>(w)};
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t w = t.v[g][i];
+                    tv[g][i] = u32x4{nibble_pair_to_bf16x2<0>(w), nibble_pair_to_bf16x2<1>(w),
+                                     nibble_pair_to_bf16x2<2>(w), nibble_pair_to_bf16x2<3>(w)};
+                }
+            } else if constexpr (Q8) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const u32x4 w = t.k[g][c >> 1];
@@ -806,7 +869,7 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
                     sc *= t.ks[g][i];
                     vsc[g][i] = ok ? t.vs[g][i] : 0.f;
                 }
-                xs[g][i] = ok ? s[g][i] * sc : -INFINITY;
+                xs[g][i] = ok ? (I4 ? s[g][i] - kcorr : s[g][i]) * sc : -INFINITY;
                 mx = fmaxf(mx, xs[g][i]);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -816,10 +879,10 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
             const float alpha = fast_exp2(m - m_new);
             m = m_new;
             l *= alpha;
+            if constexpr (I4) vsum *= alpha;
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[j] *= alpha;
         }
-        constexpr uint32_t ONES = 0x3f803f80u;
         u32x4 pb;
         if constexpr (Q8) {
 #pragma unroll
@@ -830,6 +893,10 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
                     l += p0 + p1;
                     pb[2 * g + h2] = pack_bf16x2(p0 * vsc[g][2 * h2], p1 * vsc[g][2 * h2 + 1]);
                 }
+            if constexpr (I4) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) vsum = dot2_bf16(pb[w], ONES, vsum);
+            }
         } else {
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
@@ -862,6 +929,19 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
     auto finish = [&](const Unit &x) {
         float lt = l + __shfl_xor(l, 16);
         lt += __shfl_xor(lt, 32);
+        float corr = 0.f;                       // 4-bit codes: 136 times the weights' sum (see prep_q)
+        if constexpr (I4) {
+            float vt = vsum + __shfl_xor(vsum, 16);
+            vt += __shfl_xor(vt, 32);
+            corr = I4_BIAS * vt;
+        }
+        // accumulator of dim offset e (0..7) of the lane's 8-dim run i: MFMA j = e for bf16 and 8-bit
+        // codes; for 4-bit codes MFMA j holds offset j / 2 + 4 (j % 2), so e comes from j = 2 e (e < 4) or
+        // 2 (e - 4) + 1
+        auto od = [&](int e, int i) {
+            if constexpr (I4) return acc[e < 4 ? 2 * e : 2 * (e - 4) + 1][i] - corr;
+            else return acc[e][i];
+        };
         if (n < G) {
             const int head = x.kvh * G + n;
             if (x.pslot < 0) {
@@ -870,7 +950,7 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
                 for (int i = 0; i < 4; ++i) {
                     u32x4 pk;
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) pk[w] = pack_bf16x2(acc[2 * w][i] * inv, acc[2 * w + 1][i] * inv);
+                    for (int w = 0; w < 4; ++w) pk[w] = pack_bf16x2(od(2 * w, i) * inv, od(2 * w + 1, i) * inv);
                     *(u32x4 *)((uint16_t *)out + ((int64_t)x.seq * num_heads + head) * D + 32 * b + 8 * i) = pk;
                 }
             } else {
@@ -878,8 +958,8 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float *o = ws_o + pidx * D + 32 * b + 8 * i;
-                    *(f32x4 *)o = f32x4{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
-                    *(f32x4 *)(o + 4) = f32x4{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+                    *(f32x4 *)o = f32x4{od(0, i), od(1, i), od(2, i), od(3, i)};
+                    *(f32x4 *)(o + 4) = f32x4{od(4, i), od(5, i), od(6, i), od(7, i)};
                 }
                 if (b == 0) {
                     ws_m[pidx] = m;
@@ -889,6 +969,7 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
         }
         m = M_INIT;
         l = 0.f;
+        vsum = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
@@ -1056,8 +1137,10 @@ static hipError_t launch_decode_cfg(const DecodeArgs &a, hipStream_t stream) {
         // one workgroup of nwv waves per compute unit
         const int64_t need = (units + nwv - 1) / nwv;
         const int64_t grid = need < a.compute_units ? need : a.compute_units;
-        auto kernel = !q8 ? decode_mfma_kernel<G, false, false>
-                          : a.fp8_codes ? decode_mfma_kernel<G, true, true> : decode_mfma_kernel<G, true, false>;
+        auto kernel = !q8            ? decode_mfma_kernel<G, false, false>
+                      : a.int4_codes ? decode_mfma_kernel<G, true, false, true>
+                      : a.fp8_codes  ? decode_mfma_kernel<G, true, true>
+                                     : decode_mfma_kernel<G, true, false>;
         hipLaunchKernelGGL(kernel, dim3((unsigned)grid),
                            dim3(64 * nwv), 0, stream, a.out, a.query, (const char *)a.key_cache, (const char *)a.value_cache,
                            a.block_tables, a.bt_stride, a.items, a.ctrl, a.num_kv_heads, a.num_blocks, a.log2_bs,

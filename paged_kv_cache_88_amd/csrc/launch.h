@@ -16,8 +16,9 @@ hipError_t launch_gather(void *key_out, void *value_out, const void *key_cache, 
                          const int32_t *block_table_row, int64_t len, int num_kv_heads, int row_bytes,
                          int block_size, int num_blocks, hipStream_t stream);
 
-// 8-bit caches: int8 codes (fp8 false) or OCP float8 E4M3 codes (fp8 true), one fp32 scale per row.
-hipError_t launch_store_q8(bool bf16, bool fp8, int head_dim, const void *key, const void *value, void *key_cache,
+// Quantized caches, one fp32 scale per row: format 0 int8 codes, 1 OCP float8 E4M3 codes, 2 int4 codes
+// (offset by 8, two per byte).
+hipError_t launch_store_q8(bool bf16, int format, int head_dim, const void *key, const void *value, void *key_cache,
                            void *value_cache, float *key_scale, float *value_scale, const int32_t *slot_mapping,
                            int64_t num_tokens, int num_kv_heads, int block_size, int num_blocks, hipStream_t stream);
 
@@ -53,7 +54,8 @@ struct DecodeArgs {
     float *ws_o;           // [max_items][num_heads][head_dim]
     const float *key_scale = nullptr;     // 8-bit caches only: [num_blocks][num_kv_heads][block_size]
     const float *value_scale = nullptr;
-    bool fp8_codes = false;               // 8-bit caches: E4M3 codes instead of int8
+    bool fp8_codes = false;               // quantized caches: E4M3 codes instead of int8
+    bool int4_codes = false;              // quantized caches: 4-bit codes (two per byte) instead of int8
     bool run_only = false;                // decode and reduce from a work list already in the workspace
 };
 
@@ -86,7 +88,8 @@ struct PrefillArgs {
     int causal;
     const float *key_scale = nullptr;     // 8-bit caches only: [num_blocks][num_kv_heads][block_size]
     const float *value_scale = nullptr;
-    bool fp8_codes = false;               // 8-bit caches: E4M3 codes instead of int8
+    bool fp8_codes = false;               // quantized caches: E4M3 codes instead of int8
+    bool int4_codes = false;              // quantized caches: 4-bit codes (two per byte) instead of int8
 };
 
 hipError_t launch_prefill(const PrefillArgs &a, bool bf16, int head_dim, int group, hipStream_t stream);

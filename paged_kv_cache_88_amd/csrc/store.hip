@@ -63,23 +63,27 @@ __global__ void __launch_bounds__(256) gather_kernel(u32x4 *__restrict__ key_out
     value_out[row * CHUNKS + chunk] = value_cache[src];
 }
 
-// Quantizing store ("LLM Infra 101 v0.2: KV Cache", inference-engine list, KV Quantization: K/V kept in
-// 8 bits instead of bf16). Each (token, kv head) row of D elements gets one fp32 scale and one byte per
-// element, all in fp32 with IEEE division, so codes are reproducible bit for bit:
-//   int8 (F8 false): scale = max|x| / 127, code = round_half_even(x / scale) clamped to [-127, 127];
-//   fp8 (F8 true):   scale = max|x| / 448, code = OCP float8 E4M3 of x / scale, rounded to nearest with
-//                    ties to even by v_cvt_pk_fp8_f32 (|x / scale| <= 448 up to one rounding: never NaN);
-// zero rows get scale 0 and codes 0. Codes land in the cache [num_blocks][num_kv_heads][block_size][D] at
-// the slot's row, the scale at the same (block, kv head, offset) of the [num_blocks][num_kv_heads][block_size]
+// Quantizing store ("LLM Infra 101 v0.2: KV Cache", inference-engine list, KV Quantization: K/V kept as
+// int8 or int4 instead of bf16). Each (token, kv head) row of D elements gets one fp32 scale, all in fp32
+// with IEEE division, so codes are reproducible bit for bit:
+//   int8 (FMT 0): scale = max|x| / 127, code = round_half_even(x / scale) clamped to [-127, 127], one byte;
+//   fp8 (FMT 1):  scale = max|x| / 448, code = OCP float8 E4M3 of x / scale, rounded to nearest with
+//                 ties to even by v_cvt_pk_fp8_f32 (|x / scale| <= 448 up to one rounding: never NaN), one byte;
+//   int4 (FMT 2): scale = max|x| / 7, q = round_half_even(x / scale) clamped to [-7, 7], stored as u = q + 8
+//                 in four bits, element 2j in the low half of byte j (rows of D / 2 bytes);
+// zero rows get scale 0 and q = 0. Codes land in the cache [num_blocks][num_kv_heads][block_size][row bytes]
+// at the slot's row, the scale at the same (block, kv head, offset) of the [num_blocks][num_kv_heads][block_size]
 // scale array.
 // One row per aligned group of D / 8 lanes, 8 elements per lane; the row max is a DPP butterfly.
-template <bool BF16, int D, bool F8>
+enum { STORE_INT8 = 0, STORE_FP8 = 1, STORE_INT4 = 2 };
+template <bool BF16, int D, int FMT>
 __global__ void __launch_bounds__(256) store_q8_kernel(const void *__restrict__ key, const void *__restrict__ value,
                                                        uint8_t *__restrict__ key_cache, uint8_t *__restrict__ value_cache,
                                                        float *__restrict__ key_scale, float *__restrict__ value_scale,
                                                        const int32_t *__restrict__ slot_mapping, int64_t num_rows,
                                                        int num_kv_heads, int block_size, int num_blocks) {
     constexpr int L = D / 8;               // lanes per row
+    constexpr int RB = FMT == STORE_INT4 ? D / 2 : D;     // bytes per cache row
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t row = gid / L;           // row = token * num_kv_heads + kv head; uniform over the group
     if (row >= num_rows) return;
@@ -113,10 +117,11 @@ __global__ void __launch_bounds__(256) store_q8_kernel(const void *__restrict__ 
 #pragma unroll
         for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(x[j]));
         a = group_max<L>(a);
-        const float scale = a / (F8 ? 448.0f : 127.0f);
-        uint32_t packed[2] = {0u, 0u};
-        if constexpr (F8) {
+        const float scale = a / (FMT == STORE_FP8 ? 448.0f : FMT == STORE_INT4 ? 7.0f : 127.0f);
+        uint8_t *dst = (kv ? value_cache : key_cache) + crow * RB;
+        if constexpr (FMT == STORE_FP8) {
             float qv[8];
+            uint32_t packed[2];
 #pragma unroll
             for (int j = 0; j < 8; ++j) qv[j] = a > 0.f ? x[j] / scale : 0.f;
 #pragma unroll
@@ -125,26 +130,37 @@ __global__ void __launch_bounds__(256) store_q8_kernel(const void *__restrict__ 
                 p = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4 * w + 2], qv[4 * w + 3], p, true);        // bytes 2, 3
                 packed[w] = (uint32_t)p;
             }
+            *(uint2 *)(dst + 8 * part) = make_uint2(packed[0], packed[1]);
+        } else if constexpr (FMT == STORE_INT4) {
+            uint32_t packed = 0u;                          // element 8 part + j in bits 4 j .. 4 j + 3
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float q = 0.f;
+                if (a > 0.f) q = fminf(fmaxf(__builtin_rintf(x[j] / scale), -7.f), 7.f);
+                packed |= (uint32_t)((int)q + 8) << (4 * j);
+            }
+            *(uint32_t *)(dst + 4 * part) = packed;
         } else {
+            uint32_t packed[2] = {0u, 0u};
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 float c = 0.f;
                 if (a > 0.f) c = fminf(fmaxf(__builtin_rintf(x[j] / scale), -127.f), 127.f);
                 packed[j / 4] |= ((uint32_t)(int32_t)c & 0xffu) << (8 * (j % 4));
             }
+            *(uint2 *)(dst + 8 * part) = make_uint2(packed[0], packed[1]);
         }
-        uint8_t *dst = (kv ? value_cache : key_cache) + crow * D + 8 * part;
-        *(uint2 *)dst = make_uint2(packed[0], packed[1]);
         if (part == 0) (kv ? value_scale : key_scale)[crow] = scale;
     }
 }
 
-hipError_t launch_store_q8(bool bf16, bool fp8, int head_dim, const void *key, const void *value, void *key_cache,
+hipError_t launch_store_q8(bool bf16, int format, int head_dim, const void *key, const void *value, void *key_cache,
                            void *value_cache, float *key_scale, float *value_scale, const int32_t *slot_mapping,
                            int64_t num_tokens, int num_kv_heads, int block_size, int num_blocks, hipStream_t stream) {
     const int64_t rows = num_tokens * num_kv_heads;
     const int64_t threads = rows * (head_dim / 8);
     if (threads == 0) return hipSuccess;
+    if (format < STORE_INT8 || format > STORE_INT4) return hipErrorInvalidValue;
     dim3 grid((unsigned)((threads + 255) / 256)), block(256);
     auto kc = (uint8_t *)key_cache, vc = (uint8_t *)value_cache;
 #define PKV_STORE_Q8(B, DD, F)                                                                                          \
@@ -153,13 +169,16 @@ hipError_t launch_store_q8(bool bf16, bool fp8, int head_dim, const void *key, c
 #define PKV_STORE_Q8_D(B, F)                  \
     if (head_dim == 128) PKV_STORE_Q8(B, 128, F); \
     else PKV_STORE_Q8(B, 64, F)
+#define PKV_STORE_Q8_F(B)                                                \
+    if (format == STORE_FP8) { PKV_STORE_Q8_D(B, STORE_FP8); }           \
+    else if (format == STORE_INT4) { PKV_STORE_Q8_D(B, STORE_INT4); }    \
+    else { PKV_STORE_Q8_D(B, STORE_INT8); }
     if (bf16) {
-        if (fp8) { PKV_STORE_Q8_D(true, true); }
-        else { PKV_STORE_Q8_D(true, false); }
+        PKV_STORE_Q8_F(true)
     } else {
-        if (fp8) { PKV_STORE_Q8_D(false, true); }
-        else { PKV_STORE_Q8_D(false, false); }
+        PKV_STORE_Q8_F(false)
     }
+#undef PKV_STORE_Q8_F
 #undef PKV_STORE_Q8_D
 #undef PKV_STORE_Q8
     return hipGetLastError();

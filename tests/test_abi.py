@@ -145,7 +145,8 @@ def test_decode_plan_and_run_validation(lib):
     need = lib.pkv_paged_attention_decode_workspace_size(2, 8, 2, 128, 16, 64)
     ws = ctypes.c_void_p(1 << 24)
     # (dtype, cache_kind, context_lens, B, max_len, Hq, Hkv, D, bs, workspace, bytes, stream)
-    assert plan(1, 3, FAKE, 2, 64, 8, 2, 128, 16, ws, need, None) == 1              # unknown cache kind
+    assert plan(1, 4, FAKE, 2, 64, 8, 2, 128, 16, ws, need, None) == 1              # unknown cache kind
+    assert plan(1, 3, FAKE, 2, 64, 8, 2, 64, 16, ws, need, None) == 2               # int4 cache needs D 128
     assert plan(1, 2, FAKE, 2, 64, 8, 2, 64, 16, ws, need, None) == 2               # fp8 cache needs D 128
     assert plan(0, 1, FAKE, 2, 64, 8, 2, 128, 16, ws, need, None) == 2              # 8-bit cache needs bf16
     assert plan(1, 0, None, 2, 64, 8, 2, 128, 16, ws, need, None) == 1              # null context_lens
@@ -155,7 +156,8 @@ def test_decode_plan_and_run_validation(lib):
     assert run(1, None, FAKE, FAKE, FAKE, FAKE, 4, 2, 64, 8, 2, 128, 16, 64, 0.1, ws, need, None) == 1
     assert run(1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 64, 8, 2, 128, 16, 64, 0.1, None, 0, None) == 3
     assert run(1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 65, 8, 2, 128, 16, 64, 0.1, ws, need, None) == 1   # past table
-    for name in ("pkv_paged_attention_decode_int8_run", "pkv_paged_attention_decode_fp8_run"):
+    for name in ("pkv_paged_attention_decode_int8_run", "pkv_paged_attention_decode_fp8_run",
+                 "pkv_paged_attention_decode_int4_run"):
         r8 = getattr(lib, name)
         # null scales; block size below 16
         assert r8(1, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 2, 64, 8, 2, 128, 16, 64, 0.1, ws, need, None) == 1
@@ -193,14 +195,15 @@ def test_int8_entry_points_validation(lib):
                ctypes.c_void_p(1 << 24), need, None) == 1
 
 
-def test_fp8_entry_points_validation(lib):
-    """fp8 cache calls: the same host-side checks as the int8 ones, refused before any launch."""
-    store = lib.pkv_kv_cache_store_fp8
+@pytest.mark.parametrize("kind", ["fp8", "int4"])
+def test_fp8_and_int4_entry_points_validation(lib, kind):
+    """fp8 and int4 cache calls: the same host-side checks as the int8 ones, refused before any launch."""
+    store = getattr(lib, f"pkv_kv_cache_store_{kind}")
     assert store(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 96, 16, 8, None) == 2
     assert store(1, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 2, 128, 16, 8, None) == 1
     assert store(1, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 2), FAKE, FAKE, 4, 2, 128, 16, 8, None) == 1
     assert store(1, None, None, None, None, None, None, None, 0, 2, 128, 16, 8, None) == 0
-    dec = lib.pkv_paged_attention_decode_fp8
+    dec = getattr(lib, f"pkv_paged_attention_decode_{kind}")
     assert dec(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 10, 8, 2, 128, 16, 64, 0.1, None, 0, None) == 2
     assert dec(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 10, 8, 2, 64, 16, 64, 0.1, None, 0, None) == 2
     assert dec(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 10, 8, 2, 128, 8, 64, 0.1, None, 0, None) == 2

@@ -23,7 +23,7 @@ def _decode_bytes_brute(c, code_bytes=None):
         L = int(c.context_lens[i])
         for _t in range(L):
             for _h in range(c.num_kv_heads):
-                total += 2 * (c.head_dim * e if code_bytes is None else c.head_dim * code_bytes + 4)
+                total += 2 * (c.head_dim * e if code_bytes is None else int(c.head_dim * code_bytes) + 4)
         total += 4 * len(range(0, L, c.block_size))           # block ids of blocks holding its tokens
         total += 4                                              # its context length
         total += 2 * c.num_heads * c.head_dim * (e if code_bytes is None else 2)   # query and output
@@ -38,6 +38,7 @@ def test_decode_bytes_match_brute_force():
         assert bench.decode_bytes(c) == _decode_bytes_brute(c)
         if dtype == W.BF16:
             assert bench.decode_bytes_q8(c) == _decode_bytes_brute(c, code_bytes=1)
+            assert bench.decode_bytes_q4(c) == _decode_bytes_brute(c, code_bytes=0.5)
 
 
 def test_store_bytes_match_brute_force():

@@ -1,0 +1,182 @@
+"""int4 KV cache on the GPU versus the oracle.
+
+kv_cache_store_int4 must match the oracle's quantizer bit for bit (code bytes and fp32 scales: both compute
+max|x| / 7 and round-half-even(x / scale) in fp32 with IEEE division, and pack q + 8 two per byte, element 2j
+in the low four bits). paged_attention_decode_int4 is compared with the oracle's float64 decode over the same
+codes dequantized ((u - 8) * scale): bf16 tolerance, |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise. Rows
+outside the sequences' tokens hold random code bytes and NaN scales, so any read of them shows up.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import assert_close, i32, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import paged_kv_cache_88_amd as m
+
+    m.load_library()
+    return m
+
+
+def _floats(a, dtype):
+    return W.bf16_bits_to_f32(a) if dtype == W.BF16 else np.asarray(a, np.float32)
+
+
+def garbage_int4_pool(nb, hkv, bs, d, seed, device="cuda"):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    kc = torch.randint(0, 256, (nb, hkv, bs, d // 2), dtype=torch.uint8, generator=g).to(device)
+    vc = torch.randint(0, 256, (nb, hkv, bs, d // 2), dtype=torch.uint8, generator=g).to(device)
+    ks = torch.full((nb, hkv, bs), float("nan"), dtype=torch.float32, device=device)
+    vs = torch.full((nb, hkv, bs), float("nan"), dtype=torch.float32, device=device)
+    return kc, vc, ks, vs
+
+
+def host_int4_pool(nb, hkv, bs, d):
+    return (np.zeros((nb, hkv, bs, d // 2), np.uint8), np.zeros((nb, hkv, bs, d // 2), np.uint8),
+            np.full((nb, hkv, bs), np.nan, np.float32), np.full((nb, hkv, bs), np.nan, np.float32))
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+@pytest.mark.parametrize("d", [64, 128])
+def test_store_int4_bit_exact(pkv, orc, dtype, d):
+    """Random rows (magnitudes over six decades), a zero row, a row with exact half-way quotients (scale 1),
+    padding slots; every code byte and scale equals the oracle's, untouched rows keep their bytes."""
+    rng = np.random.default_rng(17 + d)
+    nb, hkv, bs, n = 40, 3, 16, 300
+    x = rng.standard_normal((n, hkv, d)) * 10.0 ** rng.uniform(-3, 3, (n, hkv, 1))
+    x[5] = 0.0
+    x[6] = (np.arange(d) % 15) * 0.5 - 3.5          # halves from -3.5 to 3.5 at scale 1
+    x[6, :, 0] = 7.0
+    y = x[::-1] * 0.7
+    conv = (lambda a: W.f32_to_bf16_bits(a.astype(np.float32))) if dtype == W.BF16 else (lambda a: a.astype(np.float32))
+    key, val = conv(x), conv(y)
+    slots = rng.permutation(nb * bs)[:n].astype(np.int32)
+    slots[[3, 50, 299]] = -1
+    kc, vc, ks, vs = garbage_int4_pool(nb, hkv, bs, d, 2)
+    ks.fill_(-1.0)
+    vs.fill_(-2.0)
+    hk, hv, hks, hvs = (t.cpu().numpy().copy() for t in (kc, vc, ks, vs))
+    pkv.kv_cache_store_int4(to_torch(key, dtype), to_torch(val, dtype), kc, vc, ks, vs, i32(slots))
+    torch.cuda.synchronize()
+    orc.store_int4(dtype, key, val, hk, hv, hks, hvs, slots)
+    assert np.array_equal(kc.cpu().numpy(), hk)
+    assert np.array_equal(vc.cpu().numpy(), hv)
+    assert np.array_equal(ks.cpu().numpy().view(np.uint32), hks.view(np.uint32))
+    assert np.array_equal(vs.cpu().numpy().view(np.uint32), hvs.view(np.uint32))
+
+
+def store_int4_pools(pkv, orc, c):
+    """Quantize every cached row and the new tokens into a GPU pool of garbage and into host arrays."""
+    kr, vr, slots = W.cached_rows(c.pool)
+    kc, vc, ks, vs = garbage_int4_pool(c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim, c.seed)
+    hk, hv, hks, hvs = host_int4_pool(c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
+    for k_, v_, s_ in ((kr, vr, slots), (c.key, c.value, c.slot_mapping)):
+        pkv.kv_cache_store_int4(to_torch(k_, c.dtype), to_torch(v_, c.dtype), kc, vc, ks, vs, i32(s_))
+        orc.store_int4(c.dtype, k_, v_, hk, hv, hks, hvs, s_)
+    return (kc, vc, ks, vs), (hk, hv, hks, hvs)
+
+
+def run_int4_decode(pkv, orc, c, seqs=None):
+    (kc, vc, ks, vs), (hk, hv, hks, hvs) = store_int4_pools(pkv, orc, c)
+    q = to_torch(c.query, c.dtype)
+    out = torch.full_like(q, float("nan"))
+    pkv.paged_attention_decode_int4(out, q, kc, vc, ks, vs, i32(c.block_tables), i32(c.context_lens),
+                                    c.max_context_len, c.scale)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    fk = orc.dequantize_int4(hk, np.nan_to_num(hks))
+    fv = orc.dequantize_int4(hv, np.nan_to_num(hvs))
+    qf = _floats(c.query, c.dtype).astype(np.float64)
+    ref = orc.decode("f64", qf, fk, fv, c.block_tables, c.context_lens, c.scale, seqs=seqs)
+    return got, ref
+
+
+EDGE_LENS = [1, 15, 16, 17, 33, 255, 256, 257, 511, 512, 513, 1025, 3000]
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("bs", [16, 64, 256])
+def test_decode_int4_edge_lengths(pkv, orc, group, bs):
+    """Lengths around tile (32), block and part boundaries, with long contexts split over several parts
+    (their partials merged by the reduce kernel)."""
+    hkv = 2
+    nb = sum(W.blocks_for_tokens(n, bs) for n in EDGE_LENS) + 3
+    c = W.make_decode_case("int4_edge", 500 + bs + group, W.BF16, EDGE_LENS, hkv * group, hkv, 128, bs, nb)
+    got, ref = run_int4_decode(pkv, orc, c)
+    assert_close(got, ref, W.BF16, f"int4 g{group} bs{bs}")
+
+
+def test_decode_int4_empty_context_gets_zeros(pkv, orc):
+    lens = [0, 40, 0, 700]
+    nb = sum(W.blocks_for_tokens(n, 16) for n in lens) + 2
+    c = W.make_decode_case("int4_empty", 71, W.BF16, lens, 8, 2, 128, 16, nb)
+    got, ref = run_int4_decode(pkv, orc, c)
+    assert np.all(got[[0, 2]] == 0)
+    assert_close(got[[1, 3]], ref[[1, 3]], W.BF16, "int4 around empty contexts")
+
+
+def test_decode_int4_short_context_config_sampled(pkv, orc):
+    """Batch 512, lognormal contexts, block 16, 32/8 heads, shuffled 80000-block pool, in int4; the
+    oracle checks the shortest, the longest and a seeded draw of sequences."""
+    c = W.make_config(3)
+    rng = np.random.default_rng(1004)
+    seqs = np.array(sorted({int(np.argmin(c.context_lens)), int(np.argmax(c.context_lens))} |
+                           set(rng.choice(c.num_seqs, 12, replace=False).tolist())), np.int32)
+    got, ref = run_int4_decode(pkv, orc, c, seqs=seqs)
+    assert_close(got[seqs], ref, W.BF16, "int4 config")
+    assert np.isfinite(got).all()
+
+
+def test_decode_int4_long_context_config_sampled(pkv, orc):
+    """Batch 16, contexts U[16k, 32k], block 256, 64/8 heads (every sequence split into parts): two sequences
+    against the oracle, every output finite."""
+    c = W.make_config(4)
+    seqs = np.array([int(np.argmin(c.context_lens)), int(np.argmax(c.context_lens))], np.int32)
+    got, ref = run_int4_decode(pkv, orc, c, seqs=seqs)
+    assert_close(got[seqs], ref, W.BF16, "int4 long contexts")
+    assert np.isfinite(got).all()
+
+
+def test_decode_int4_plan_run_equals_whole_call(pkv, orc):
+    """paged_attention_decode_plan(cache="int4") once, then two runs over different caches: each equals the
+    whole int4 call bit for bit."""
+    lens = [700, 33, 0, 1300, 512, 9, 2047, 1, 64]
+    nb = sum(W.blocks_for_tokens(n, 16) for n in lens) + 4
+    c0 = W.make_decode_case("int4_plan", 80, W.BF16, lens, 32, 8, 128, 16, nb)
+    cl = i32(c0.context_lens)
+    ws = torch.empty(pkv.decode_workspace_size(c0.num_seqs, 32, 8, 128, 16, c0.max_context_len), dtype=torch.uint8,
+                     device="cuda")
+    pkv.paged_attention_decode_plan(cl, c0.max_context_len, 32, 8, 128, 16, ws, cache="int4")
+    for k in range(2):
+        c = W.make_decode_case("int4_plan", 81 + k, W.BF16, lens, 32, 8, 128, 16, nb)
+        (kc, vc, ks, vs), _ = store_int4_pools(pkv, orc, c)
+        q = to_torch(c.query, c.dtype)
+        bt = i32(c.block_tables)
+        out = torch.full_like(q, float("nan"))
+        pkv.paged_attention_decode_int4_run(out, q, kc, vc, ks, vs, bt, c.max_context_len, c.scale, ws)
+        whole = torch.full_like(q, float("nan"))
+        pkv.paged_attention_decode_int4(whole, q, kc, vc, ks, vs, bt, cl, c.max_context_len, c.scale,
+                                        workspace=torch.empty_like(ws))
+        torch.cuda.synchronize()
+        assert torch.equal(out, whole), f"int4 layer {k}: run differs from the whole call"
+
+
+def test_decode_int4_close_to_bf16(pkv, orc):
+    """A sanity bound, not parity: against attention over the unquantized bf16 cache, N(0, 1) data moves by
+    at most max|x| / 14 per element (about 0.2), so single-token contexts (output = that token's V) move by
+    about that much and long contexts, which average many rows, by much less."""
+    c = W.make_decode_case("int4_vs_bf16", 13, W.BF16, [700, 64, 2048, 1], 32, 8, 128, 16, 400)
+    got, _ = run_int4_decode(pkv, orc, c)
+    kc, vc = c.pool.dense()
+    orc.store(c.dtype, c.key, c.value, kc, vc, c.slot_mapping)
+    ref = orc.decode(c.dtype, c.query, kc, vc, c.block_tables, c.context_lens, c.scale)
+    v_step = np.abs(_floats(c.value, c.dtype)).max(axis=-1) / 7.0          # [B, Hkv]: the new token's V scale
+    assert np.abs(got[3] - ref[3]).max() <= (v_step[3].max() / 2) * 1.05 + 2e-2
+    assert np.abs(got[:3] - ref[:3]).mean() < 0.05
