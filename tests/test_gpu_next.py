@@ -192,17 +192,20 @@ def _replays_match_eager(step, refresh, outs, reps=4):
             assert torch.equal(a, b), f"replay {rep} differs from eager"
 
 
-def test_fp8_decode_step_in_hip_graph(pkv):
-    """fp8 store + fp8 decode captured once and replayed with new queries and context lengths: the plan
+@pytest.mark.parametrize("kind", ["fp8", "int4"])
+def test_quantized_decode_step_in_hip_graph(pkv, kind):
+    """fp8 (or int4) store + decode captured once and replayed with new queries and context lengths: the plan
     kernel and the decode kernel's unit counter reset on the device, so every replay equals eager."""
     c = W.make_decode_case("graph_fp8", 6, W.BF16, [700, 33, 1300, 512, 9, 2047], 32, 8, 128, 16, 400)
     kr, vr, slots = W.cached_rows(c.pool)
-    shape = (c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
+    store = getattr(pkv, f"kv_cache_store_{kind}")
+    decode = getattr(pkv, f"paged_attention_decode_{kind}")
+    shape = (c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim // 2 if kind == "int4" else c.head_dim)
     kc = torch.zeros(shape, dtype=torch.uint8, device="cuda")
     vc = torch.zeros_like(kc)
     ks = torch.zeros(shape[:3], dtype=torch.float32, device="cuda")
     vs = torch.zeros_like(ks)
-    pkv.kv_cache_store_fp8(to_torch(kr, c.dtype), to_torch(vr, c.dtype), kc, vc, ks, vs, i32(slots))
+    store(to_torch(kr, c.dtype), to_torch(vr, c.dtype), kc, vc, ks, vs, i32(slots))
     q = to_torch(c.query, c.dtype)
     kn, vn = to_torch(c.key, c.dtype), to_torch(c.value, c.dtype)
     bt, cl, sm = i32(c.block_tables), i32(c.context_lens), i32(c.slot_mapping)
@@ -210,8 +213,8 @@ def test_fp8_decode_step_in_hip_graph(pkv):
     ws = torch.empty(pkv.decode_workspace_size(c.num_seqs, 32, 8, 128, 16, 2048), dtype=torch.uint8, device="cuda")
 
     def step():
-        pkv.kv_cache_store_fp8(kn, vn, kc, vc, ks, vs, sm)
-        pkv.paged_attention_decode_fp8(out, q, kc, vc, ks, vs, bt, cl, 2048, c.scale, workspace=ws)
+        store(kn, vn, kc, vc, ks, vs, sm)
+        decode(out, q, kc, vc, ks, vs, bt, cl, 2048, c.scale, workspace=ws)
 
     rng = np.random.default_rng(1)
 
