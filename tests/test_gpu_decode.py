@@ -151,9 +151,9 @@ def test_empty_context_gives_zeros(pkv, orc):
     assert_close(got, ref, W.BF16, "empty")
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4])
+@pytest.mark.parametrize("cfg", [2, 3, 4], ids=lambda n: W.CONFIGS[n].__name__)
 def test_config_full_size_sampled(pkv, orc, cfg):
-    """Full-size configs in the launch configuration the bench times; the oracle checks a sample of
+    """The benchmark's decode workloads at full size, in the launch configuration the bench times; the oracle checks a sample of
     sequences (the shortest, the longest and a seeded draw), every head and dimension."""
     c = W.make_config(cfg)
     got, _, _ = run_decode_case(pkv, c)

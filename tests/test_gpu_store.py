@@ -52,9 +52,10 @@ def test_store_empty_and_all_padding(pkv, orc):
                        torch.empty(0, dtype=torch.int32, device="cuda"))
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5], ids=lambda n: W.CONFIGS[n].__name__)
 def test_store_bit_exact_configs(pkv, orc, cfg):
-    """The configs' store step (one token per sequence; the whole chunk for prefill) at full size."""
+    """The store step of each benchmark workload (one token per sequence; the whole chunk for prefill) at full
+    size."""
     c = W.make_config(cfg)
     kc_h, vc_h = c.pool.dense()
     orc.store(c.dtype, c.key, c.value, kc_h, vc_h, c.slot_mapping)
