@@ -292,6 +292,54 @@ def check_gather_matches_numpy_indexing(orc, seed=42):
     assert np.array_equal(vo.astype(np.float64), numpy_gather(vc, bt[0], 14))
 
 
+def _sentinel_pool(nb, hkv, bs, d):
+    """K holds 1, 2, 3, ... and V holds -1, -2, -3, ... in storage order: every element of the pool is
+    distinct, so each block's contents name the block they came from. Small integers are exact in bf16."""
+    n = nb * hkv * bs * d
+    k = np.arange(1, n + 1, dtype=np.float32).reshape(nb, hkv, bs, d)
+    return k, -k
+
+
+def _copy_blocks_case(orc, dtype, pairs, holds, nb=5, hkv=2, bs=2, d=4):
+    """Copy ``pairs`` in a sentinel pool; afterwards block b of both caches must hold what block holds[b]
+    held before (worked out by hand from the pair list)."""
+    from workloads import BF16, f32_to_bf16_bits
+
+    k0, v0 = _sentinel_pool(nb, hkv, bs, d)
+    if dtype == BF16:
+        kc, vc = f32_to_bf16_bits(k0), f32_to_bf16_bits(v0)
+    else:
+        kc, vc = k0.copy(), v0.copy()
+    before_k, before_v = kc.copy(), vc.copy()
+    orc.copy_blocks(dtype, kc, vc, np.array(pairs, np.int32))
+    for b, src in enumerate(holds):
+        assert np.array_equal(kc[b], before_k[src]), f"K block {b} should hold old block {src}"
+        assert np.array_equal(vc[b], before_v[src]), f"V block {b} should hold old block {src}"
+
+
+def check_copy_blocks_worked_cases(orc):
+    """Copy-on-write of whole blocks ("推理运行时", section Prefix cache 与 copy-on-write: a branch that
+    writes into a shared block first gets a private copy of it). Pool of 5 blocks x 2 kv heads x 2 rows x
+    4 dims with every element distinct.
+    * pairs (3 -> 1), (0 -> 2): block 1 now holds old block 3 and block 2 old block 0; blocks 0, 3 and 4
+      (the sources and the untouched neighbour of both destinations) keep their contents; both kv heads
+      and both K and V move.
+    * pairs (1 -> 0), (0 -> 2): block 0 is written by the first pair and read by the second; the copy
+      reads every source before writing, so block 2 gets old block 0, not old block 1.
+    Checked for float32 and for bf16 bit patterns (2-byte elements)."""
+    from workloads import BF16
+
+    for dt in (F32, BF16):
+        _copy_blocks_case(orc, dt, [[3, 1], [0, 2]], [0, 3, 0, 3, 4])
+        _copy_blocks_case(orc, dt, [[1, 0], [0, 2]], [1, 1, 0, 3, 4])
+        _copy_blocks_case(orc, dt, [[4, 3]], [0, 1, 2, 4, 4])
+    # one element written out: K of block 1, kv head 1, row 0, dim 2 after (3 -> 1) is old K[3, 1, 0, 2],
+    # the element at flat index ((3 * 2 + 1) * 2 + 0) * 4 + 2 = 58, which holds 59
+    k, v = _sentinel_pool(5, 2, 2, 4)
+    orc.copy_blocks(F32, k, v, np.array([[3, 1]], np.int32))
+    assert k[1, 1, 0, 2] == 59.0 and v[1, 1, 0, 2] == -59.0
+
+
 def check_int8_power_of_two_scale(orc):
     """Rows whose largest magnitude is 127 * 2^-3 (a negative element) and whose other elements are integer
     multiples of 2^-3: scale = 2^-3 exactly, codes = the integers, dequantized values = the inputs."""
@@ -597,6 +645,7 @@ ALL_CHECKS = [
     check_decode_is_last_prefill_row,
     check_chunk_split_invariance,
     check_store_places_rows,
+    check_copy_blocks_worked_cases,
     check_int8_power_of_two_scale,
     check_int8_ties_to_even,
     check_int8_zero_row_bound_and_symmetry,

@@ -80,6 +80,16 @@ MUTANTS = {
                                   "int u = (d % 2) ? (byte & 15) : (byte >> 4);"),
     "int4_dequant_no_offset": ("out[r * dim + d] = (double)(u - 8) * (double)scales[r];",
                                "out[r * dim + d] = (double)u * (double)scales[r];"),
+    "copy_blocks_key_only": ("memcpy((char *)value_cache + (size_t)pairs[2 * k + 1] * block_bytes, tmp + (2 * (size_t)k + 1) * block_bytes, block_bytes);",
+                             ";"),
+    "copy_blocks_key_into_source": ("memcpy((char *)key_cache + (size_t)pairs[2 * k + 1] * block_bytes, tmp",
+                                    "memcpy((char *)key_cache + (size_t)pairs[2 * k] * block_bytes, tmp"),
+    "copy_blocks_one_kv_head": ("size_t block_bytes = (size_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype);",
+                                "size_t block_bytes = (size_t)block_size * head_dim * elem_bytes(dtype);"),
+    "copy_blocks_no_snapshot": ("tmp + (2 * (size_t)k) * block_bytes, block_bytes);",
+                                "(char *)key_cache + (size_t)pairs[2 * k] * block_bytes, block_bytes);"),
+    "copy_blocks_four_byte_elements": ("size_t block_bytes = (size_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype);",
+                                       "size_t block_bytes = (size_t)num_kv_heads * block_size * head_dim * 4;"),
     "int4_store_scale_at_offset": ("value_cache + crow * row_bytes, value_scale + crow);",
                                    "value_cache + crow * row_bytes, value_scale + pos);"),
 }
