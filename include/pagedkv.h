@@ -321,8 +321,10 @@ pkv_status pkv_paged_attention_decode_int4(pkv_dtype dtype, void *out, const voi
  *   pkv_paged_attention_decode (no cache or output pointers are taken).
  * run: the arguments of pkv_paged_attention_decode (or of its _int8 / _fp8 / _int4 form) without context_lens. It
  *   needs a workspace planned with the same num_seqs, max_context_len, num_heads, num_kv_heads, head_dim,
- *   block_size and context_lens (the caller's contract: the work list records token ranges; a run over a
- *   stale plan attends over the planned lengths), and reads the plan in stream order. A whole decode call
+ *   block_size, cache kind and query dtype, and the same context_lens (the caller's contract for the lengths:
+ *   the work list records token ranges; a run over a stale plan attends over the planned lengths), and reads
+ *   the plan in stream order. A run whose sizes differ from its plan's is detected on the device: it writes
+ *   nothing and raises the workspace's run status (pkv_paged_attention_decode_status). A whole decode call
  *   leaves the same plan in its workspace.
  * Source: the attention metadata of the pages above, built once per step; the work list as for
  * pkv_paged_attention_decode.
@@ -361,6 +363,19 @@ pkv_status pkv_paged_attention_decode_int4_run(pkv_dtype dtype, void *out, const
                                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                                int64_t num_blocks, float scale, void *workspace,
                                                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_attention_decode_status: enqueues on `stream` a copy of the workspace's run status into *status (device
+ * memory or pinned host memory; 4 bytes): 0 when every run since the workspace's last plan matched that plan,
+ * 1 when a run found the workspace planned for other sizes. A plan (or whole decode call) records in the
+ * workspace what it was made for: num_seqs, max_context_len, num_heads, num_kv_heads, head_dim, block_size,
+ * the cache kind and the query dtype. A run compares that record with its own arguments before it reads the
+ * work list and, on any difference, writes nothing (out keeps its contents) and sets the status to 1; the next
+ * plan resets it to 0. Read the status after the run in stream order.
+ * Source: none on the pages; this guards the plan/run split above (a run over a plan for other sizes would
+ * otherwise index the workspace with another layout).
+ */
+pkv_status pkv_paged_attention_decode_status(const void *workspace, int32_t *status, hipStream_t stream);
 
 /* Message of the calling thread's last non-OK status ("" if none). Owned by the library. */
 const char *pkv_last_error(void);

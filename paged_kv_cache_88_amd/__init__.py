@@ -92,6 +92,8 @@ def load_library(path: str = LIB_PATH):
                  "pkv_bm_block_table", "pkv_bm_slot_mapping", "pkv_bm_take_copies", "pkv_bm_usage"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pkv_bm_last_error.restype = ctypes.c_char_p
+    lib.pkv_paged_attention_decode_status.argtypes = [P, P, P]
+    lib.pkv_paged_attention_decode_status.restype = ctypes.c_int
     lib.pkv_paged_attention_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.pkv_paged_attention_decode_workspace_size.restype = SZ
     lib.pkv_last_error.restype = ctypes.c_char_p
@@ -257,6 +259,18 @@ def paged_attention_decode_run(out, query, key_cache, value_cache, block_tables,
 
 
 _CODE_DTYPES = {"int8": (torch.int8,), "fp8": (torch.uint8, torch.float8_e4m3fn), "int4": (torch.uint8,)}
+
+
+def paged_attention_decode_status(workspace, status=None, stream=None):
+    """Enqueue a copy of ``workspace``'s run status into ``status`` (int32 [1] on the device; allocated when
+    None) and return it: 0 when every run since the last plan matched that plan's sizes, 1 when a run found a
+    plan for other sizes (and wrote nothing)."""
+    _dev(workspace)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=workspace.device)
+    _dev(status)
+    _check(load_library().pkv_paged_attention_decode_status(_ptr(workspace), _ptr(status), _stream(stream)))
+    return status
 
 
 def _cache_dims(kind, key_cache):

@@ -214,7 +214,7 @@ pkv_status decode_args(pkv::DecodeArgs &a, pkv_dtype dtype, void *out, const voi
                        int32_t block_table_stride, const int32_t *context_lens, int32_t num_seqs,
                        int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int64_t num_blocks, float scale, void *workspace, size_t workspace_bytes,
-                       DecodeMode mode = DECODE_CALL) {
+                       DecodeMode mode = DECODE_CALL, int cache_kind = PKV_CACHE_ELEMENTS) {
     pkv_status st = check_common(dtype, num_kv_heads, head_dim, block_size, num_blocks);
     if (st != PKV_OK) return st;
     st = check_heads(num_heads, num_kv_heads);
@@ -270,6 +270,8 @@ pkv_status decode_args(pkv::DecodeArgs &a, pkv_dtype dtype, void *out, const voi
     a.ws_l = (float *)((char *)workspace + plan.off_l);
     a.ws_o = (float *)((char *)workspace + plan.off_o);
     a.run_only = mode == DECODE_RUN_ONLY;
+    a.key = pkv::PlanKey{{pkv::PLAN_KEY_MAGIC, num_seqs, max_context_len, num_kv_heads, num_heads, head_dim,
+                          a.log2_bs, cache_kind | ((int)dtype << 4)}};
     return ok();
 }
 
@@ -331,9 +333,10 @@ pkv_status decode_q8(int format, const char *what, pkv_dtype dtype, void *out, c
     REQUIRE(block_size >= 16, PKV_EUNSUPPORTED, "quantized-cache decode needs block_size >= 16 (got %d)",
             block_size);
     pkv::DecodeArgs a{};
+    const int kind = format == Q_FP8 ? PKV_CACHE_FP8 : format == Q_INT4 ? PKV_CACHE_INT4 : PKV_CACHE_INT8;
     pkv_status st = decode_args(a, dtype, out, query, key_cache, value_cache, block_tables, block_table_stride,
                                 context_lens, num_seqs, max_context_len, num_heads, num_kv_heads, head_dim, block_size,
-                                num_blocks, scale, workspace, workspace_bytes, mode);
+                                num_blocks, scale, workspace, workspace_bytes, mode, kind);
     if (st != PKV_OK || num_seqs == 0) return st;
     REQUIRE(key_scale && value_scale, PKV_EINVAL, "null scale array");
     REQUIRE(((uintptr_t)key_scale & 15u) == 0 && ((uintptr_t)value_scale & 15u) == 0, PKV_EINVAL,
@@ -432,7 +435,7 @@ pkv_status pkv_paged_attention_decode_plan(pkv_dtype dtype, int32_t cache_kind, 
     const pkv_status st = decode_args(a, dtype, nullptr, nullptr, nullptr, nullptr, nullptr,
                                       (max_context_len + block_size - 1) / (block_size > 0 ? block_size : 1),
                                       context_lens, num_seqs, max_context_len, num_heads, num_kv_heads, head_dim,
-                                      block_size, 1, 1.0f, workspace, workspace_bytes, DECODE_PLAN_ONLY);
+                                      block_size, 1, 1.0f, workspace, workspace_bytes, DECODE_PLAN_ONLY, cache_kind);
     if (st != PKV_OK || num_seqs == 0) return st;
     const bool mfma = q8 || pkv::decode_uses_mfma(dtype == PKV_BF16, head_dim, num_heads / num_kv_heads, a.log2_bs);
     return hip_status(pkv::launch_decode_plan(a, mfma, q8, stream), "paged_attention_decode_plan launch");
@@ -493,6 +496,14 @@ pkv_status pkv_paged_attention_decode_int4_run(pkv_dtype dtype, void *out, const
                      key_scale, value_scale, block_tables, block_table_stride, nullptr, num_seqs, max_context_len,
                      num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace, workspace_bytes,
                      stream, DECODE_RUN_ONLY);
+}
+
+pkv_status pkv_paged_attention_decode_status(const void *workspace, int32_t *status, hipStream_t stream) {
+    REQUIRE(workspace && status, PKV_EINVAL, "null pointer argument");
+    REQUIRE(((uintptr_t)workspace & 255u) == 0, PKV_EINVAL, "workspace must be 256-byte aligned");
+    return hip_status(hipMemcpyAsync(status, (const int *)workspace + pkv::CTRL_ERR, sizeof(int32_t), hipMemcpyDefault,
+                                     stream),
+                      "paged_attention_decode_status copy");
 }
 
 }  // extern "C"

@@ -67,6 +67,17 @@ struct TileRegs {
     bool valid[S::R];
 };
 
+// A run trusts its work list only when the plan's key in the control block equals its own (same sizes, so
+// the same workspace layout and unit bounds). The words are wave-uniform scalar loads; on a mismatch the
+// kernel raises the error word and returns before any other memory access.
+__device__ __forceinline__ bool plan_key_ok(int *ctrl, const PlanKey &key) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ok &= ctrl[CTRL_KEY + i] == key.w[i];
+    if (!ok && threadIdx.x == 0) ctrl[CTRL_ERR] = 1;
+    return ok;
+}
+
 constexpr int PLAN_THREADS = 1024;
 constexpr int PLAN_WAVES = PLAN_THREADS / 64;
 constexpr int PLAN_BUCKETS = 64;
@@ -133,7 +144,7 @@ constexpr int PLAN_REG = 4;
 __global__ void __launch_bounds__(PLAN_THREADS)
 decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int max_context_len, int num_kv_heads,
                    int workers, int min_strata, int max_tiles, int min_tiles,
-                   int4 *__restrict__ items, int4 *__restrict__ seq_info, int *__restrict__ ctrl) {
+                   int4 *__restrict__ items, int4 *__restrict__ seq_info, int *__restrict__ ctrl, PlanKey key) {
     __shared__ int s_wave[PLAN_WAVES];
     __shared__ int hist[PLAN_BUCKETS];
     __shared__ int offs[PLAN_BUCKETS];
@@ -224,7 +235,12 @@ decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int m
         const int64_t grown = ((int64_t)target * H * carry + cap - 1) / cap;
         target = (int)(grown > target + 1 ? (grown < max_tiles ? grown : max_tiles) : target + 1);
     }
-    if (tid == 0) ctrl[0] = carry;
+    if (tid == 0) {
+        ctrl[CTRL_PARTS] = carry;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) ctrl[CTRL_KEY + w] = key.w[w];
+        ctrl[CTRL_ERR] = 0;
+    }
     my_max = wave_total_max(my_max);
     if (wave_lead) atomicMax(&s_maxlen, my_max);
     __syncthreads();
@@ -264,10 +280,11 @@ template <bool BF16, int D, int G, int NV_, int R_, int NW_>
 __global__ void __launch_bounds__(64 * NW_)
 decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x4 *__restrict__ key_cache,
               const u32x4 *__restrict__ value_cache, const int32_t *__restrict__ block_tables, int bt_stride,
-              const int4 *__restrict__ items, const int *__restrict__ ctrl, int num_kv_heads,
+              const int4 *__restrict__ items, int *__restrict__ ctrl, PlanKey key, int num_kv_heads,
               int64_t num_blocks, int log2_bs, float scale_log2e,
               float *__restrict__ ws_m, float *__restrict__ ws_l, float *__restrict__ ws_o) {
     using S = DecodeShape<BF16, D, G, NV_, R_, NW_>;
+    if (!plan_key_ok(ctrl, key)) return;
     constexpr int NV = S::NV, LPT = S::LPT, RPW = S::RPW, R = S::R, TILE = S::TILE, EPL = S::EPL, VEC = S::VEC;
     constexpr int NW = S::NW;
 
@@ -277,7 +294,7 @@ decode_kernel(void *__restrict__ out, const void *__restrict__ query, const u32x
 
     // unit in longest-first order; workgroups past the list exit
     const int unit = blockIdx.x;
-    if (unit >= ctrl[0] * num_kv_heads) return;
+    if (unit >= ctrl[CTRL_PARTS] * num_kv_heads) return;
     const int4 item = items[unit / num_kv_heads];
     const int kvh = unit % num_kv_heads;
     const int seq = item.x, start = item.y, ntok = item.z, pslot = item.w;
@@ -652,11 +669,12 @@ template <int G, bool Q8, bool F8, bool I4 = false, int NWV = Q8 ? DECODE_CU_WAV
 __global__ void __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const char *__restrict__ key_cache,
                    const char *__restrict__ value_cache, const int32_t *__restrict__ block_tables, int bt_stride,
-                   const int4 *__restrict__ items, const int *__restrict__ ctrl, int num_kv_heads,
+                   const int4 *__restrict__ items, int *__restrict__ ctrl, PlanKey key, int num_kv_heads,
                    int64_t num_blocks, int log2_bs, float scale_log2e,
                    float *__restrict__ ws_m, float *__restrict__ ws_l, float *__restrict__ ws_o,
                    const float *__restrict__ key_scale, const float *__restrict__ value_scale) {
     static_assert(G >= 1 && G <= 16, "query heads per kv head");
+    if (!plan_key_ok(ctrl, key)) return;
     constexpr int D = 128, CH = D / 8;        // 16-byte chunks of a bf16 row
     static_assert(!I4 || (Q8 && !F8), "4-bit codes use the quantized-cache path");
     constexpr int RB = I4 ? D / 2 : Q8 ? D : 2 * D;     // bytes per cache row
@@ -665,7 +683,7 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
     const int lane = threadIdx.x & 63, n = lane & 15, b = lane >> 4;
     const int num_heads = num_kv_heads * G;
     const int bs_mask = (1 << log2_bs) - 1;
-    const int nunits = ctrl[0] * num_kv_heads;
+    const int nunits = ctrl[CTRL_PARTS] * num_kv_heads;
     // Units are dealt to the C workgroups (one per compute unit) from the longest-first list in strata
     // of C: in stratum k workgroup c takes unit k C + c for even k and k C + C - 1 - c for odd k (snake
     // order, so the long units of one stratum pair with the short ones of the next), except that a
@@ -1048,10 +1066,12 @@ constexpr int REDUCE_THREADS = 256;
 template <bool BF16, int D>
 __global__ void __launch_bounds__(REDUCE_THREADS)
 decode_reduce_kernel(void *__restrict__ out, const int4 *__restrict__ seq_info, int num_heads, int hpb,
-                     const float *__restrict__ ws_m, const float *__restrict__ ws_l, const float *__restrict__ ws_o) {
+                     const float *__restrict__ ws_m, const float *__restrict__ ws_l, const float *__restrict__ ws_o,
+                     int *__restrict__ ctrl, PlanKey key) {
     constexpr int DG = D / 4, SLOTS = REDUCE_THREADS / DG;          // SLOTS = head slots x part lanes
     __shared__ f32x4 s_o[SLOTS][DG];
     __shared__ float s_l[SLOTS], s_m[SLOTS];
+    if (!plan_key_ok(ctrl, key)) return;
     const int seq = blockIdx.y;
     const int4 si = seq_info[seq];
     const int nparts = si.y;
@@ -1118,7 +1138,7 @@ static hipError_t launch_plan(const DecodeArgs &a, bool mfma, bool q8, hipStream
     const int workers = mfma ? a.compute_units * (q8 ? DECODE_CU_WAVES_Q8 : DECODE_CU_WAVES_BF16) : a.workers;
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, a.context_lens, a.num_seqs,
                        a.max_context_len, a.num_kv_heads, workers, a.min_strata, a.max_part_tiles, a.min_part_tiles,
-                       a.items, a.seq_info, a.ctrl);
+                       a.items, a.seq_info, a.ctrl, a.key);
     return hipGetLastError();
 }
 
@@ -1143,12 +1163,12 @@ static hipError_t launch_decode_cfg(const DecodeArgs &a, hipStream_t stream) {
                                      : decode_mfma_kernel<G, true, false>;
         hipLaunchKernelGGL(kernel, dim3((unsigned)grid),
                            dim3(64 * nwv), 0, stream, a.out, a.query, (const char *)a.key_cache, (const char *)a.value_cache,
-                           a.block_tables, a.bt_stride, a.items, a.ctrl, a.num_kv_heads, a.num_blocks, a.log2_bs,
+                           a.block_tables, a.bt_stride, a.items, a.ctrl, a.key, a.num_kv_heads, a.num_blocks, a.log2_bs,
                            a.scale_log2e, a.ws_m, a.ws_l, a.ws_o, a.key_scale, a.value_scale);
     } else {
         hipLaunchKernelGGL((decode_kernel<BF16, D, G, NV, R, NW>), dim3((unsigned)units), dim3(64 * NW), 0, stream,
                            a.out, a.query, (const u32x4 *)a.key_cache, (const u32x4 *)a.value_cache, a.block_tables,
-                           a.bt_stride, a.items, a.ctrl, a.num_kv_heads, a.num_blocks, a.log2_bs, a.scale_log2e,
+                           a.bt_stride, a.items, a.ctrl, a.key, a.num_kv_heads, a.num_blocks, a.log2_bs, a.scale_log2e,
                            a.ws_m, a.ws_l, a.ws_o);
     }
     e = hipGetLastError();
@@ -1158,7 +1178,8 @@ static hipError_t launch_decode_cfg(const DecodeArgs &a, hipStream_t stream) {
     int hpb = 8;
     while (hpb > 1 && (int64_t)((num_heads + hpb - 1) / hpb) * a.num_seqs < 2048) hpb >>= 1;
     hipLaunchKernelGGL((decode_reduce_kernel<BF16, D>), dim3((num_heads + hpb - 1) / hpb, a.num_seqs),
-                       dim3(REDUCE_THREADS), 0, stream, a.out, a.seq_info, num_heads, hpb, a.ws_m, a.ws_l, a.ws_o);
+                       dim3(REDUCE_THREADS), 0, stream, a.out, a.seq_info, num_heads, hpb, a.ws_m, a.ws_l, a.ws_o,
+                       a.ctrl, a.key);
     return hipGetLastError();
 }
 

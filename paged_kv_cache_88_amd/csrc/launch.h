@@ -25,6 +25,19 @@ hipError_t launch_store_q8(bool bf16, int format, int head_dim, const void *key,
 hipError_t launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *pairs, int num_pairs, int64_t block_bytes,
                               int num_blocks, hipStream_t stream);
 
+// What a decode plan was made for: the sizes that fix the workspace layout and the unit list (num_seqs,
+// max_context_len, num_kv_heads, num_heads, head_dim, log2 block_size) and the cache it sizes parts for
+// (cache kind | query dtype << 4), after a magic word. The plan kernel writes it into the workspace's control
+// block; the decode and reduce kernels compare it with their own before touching anything else and, on a
+// mismatch, set the control block's error word and exit.
+struct PlanKey {
+    int w[8];
+};
+constexpr int PLAN_KEY_MAGIC = 0x504b5650;
+constexpr int CTRL_PARTS = 0;          // int32 words of the 256-byte control block
+constexpr int CTRL_KEY = 8;            // [8, 16): the plan's key
+constexpr int CTRL_ERR = 16;           // 0 after a plan; 1 once a run found a key other than its own
+
 struct DecodeArgs {
     void *out;
     const void *query;
@@ -57,6 +70,7 @@ struct DecodeArgs {
     bool fp8_codes = false;               // quantized caches: E4M3 codes instead of int8
     bool int4_codes = false;              // quantized caches: 4-bit codes (two per byte) instead of int8
     bool run_only = false;                // decode and reduce from a work list already in the workspace
+    PlanKey key{};                        // written by the plan, checked by the run
 };
 
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, int head_dim, int group, hipStream_t stream);

@@ -65,6 +65,22 @@ def assert_close(gpu, ref, dtype, what=""):
                              f"ref={ref[i]}; max abs err {err.max():.3g}")
 
 
+def decode_workers(kind="bf16"):
+    """Resident waves the decode plan sizes parts for on this GPU: 4 per compute unit for the matrix-core
+    kernel over a bf16 cache, 8 over a quantized cache, and 8 (at most 2048) for the vector-ALU kernel."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return {"bf16": 4 * cus, "q8": 8 * cus, "valu": min(8 * cus, 2048)}[kind]
+
+
+def assert_rel_norm(got, ref, bound=1e-2, what=""):
+    """||gpu - ref|| / ||ref|| <= bound over all elements: bf16 rounds each softmax weight and each output to
+    8 significant bits (relative error <= 2^-9 each), which keeps the norm of the error within ~2^-8 of the
+    norm of the output however small the elements are."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    r = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    assert r <= bound, f"{what}: relative error norm {r:.3g} > {bound}"
+
+
 def run_decode_case(pkv, c: W.DecodeCase, store=True, device="cuda"):
     """Store the new token (HIP), then decode (HIP). Returns (out as float64 numpy, kc, vc)."""
     kc, vc = device_pool(c.pool, device)

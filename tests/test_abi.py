@@ -164,6 +164,15 @@ def test_decode_plan_and_run_validation(lib):
         assert r8(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2, 64, 8, 2, 128, 8, 64, 0.1, ws, need, None) == 2
 
 
+def test_decode_status_validation(lib):
+    """The run-status copy refuses null and misaligned pointers before enqueuing anything."""
+    st = lib.pkv_paged_attention_decode_status
+    assert st(None, FAKE, None) == 1
+    assert st(FAKE, None, None) == 1
+    assert st(ctypes.c_void_p((1 << 20) + 64), FAKE, None) == 1
+    assert "256-byte" in _err(lib)
+
+
 def test_binding_fails_loudly_without_library(pkv, tmp_path):
     saved = pkv._lib
     try:

@@ -10,8 +10,9 @@ import numpy as np
 import pytest
 import torch
 
+import needles as N
 import workloads as W
-from gpu_util import assert_close, i32, to_torch
+from gpu_util import assert_close, assert_rel_norm, decode_workers, i32, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -129,16 +130,23 @@ def test_decode_fp8_edge_lengths(pkv, orc, group, bs):
     assert_close(got, ref, W.BF16, f"fp8 g{group} bs{bs}")
 
 
-def test_decode_fp8_short_context_config_sampled(pkv, orc):
-    """Batch 512, lognormal contexts, block 16, 32/8 heads, shuffled 80000-block pool, in fp8; the
-    oracle checks the shortest, the longest and a seeded draw of sequences."""
+def test_decode_fp8_short_context_config(pkv, orc):
+    """Batch 512, lognormal contexts, block 16, 32/8 heads, shuffled 80000-block pool, in fp8: every output
+    against the oracle."""
     c = W.make_config(3)
-    rng = np.random.default_rng(1004)
-    seqs = np.array(sorted({int(np.argmin(c.context_lens)), int(np.argmax(c.context_lens))} |
-                           set(rng.choice(c.num_seqs, 12, replace=False).tolist())), np.int32)
-    got, ref = run_fp8_decode(pkv, orc, c, seqs=seqs)
-    assert_close(got[seqs], ref, W.BF16, "fp8 config")
-    assert np.isfinite(got).all()
+    got, ref = run_fp8_decode(pkv, orc, c)
+    assert_close(got, ref, W.BF16, "fp8 config")
+    assert_rel_norm(got, ref, what="fp8 config")
+
+
+def test_decode_fp8_long_context_planted_keys(pkv, orc):
+    """The long-context workload in fp8 with two dominant keys planted per query head (exact in E4M3: one
+    magnitude per row): every output against the oracle."""
+    c = W.make_config(4)
+    W.plant_dominant_keys(c, N.needle_positions(c, np.random.default_rng(49), decode_workers("q8")))
+    got, ref = run_fp8_decode(pkv, orc, c)
+    assert_close(got, ref, W.BF16, "fp8 long contexts, planted keys")
+    assert_rel_norm(got, ref, what="fp8 long contexts, planted keys")
 
 
 def test_decode_fp8_close_to_bf16(pkv, orc):

@@ -10,8 +10,9 @@ import numpy as np
 import pytest
 import torch
 
+import needles as N
 import workloads as W
-from gpu_util import assert_close, i32, to_torch
+from gpu_util import assert_close, assert_rel_norm, decode_workers, i32, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -122,26 +123,24 @@ def test_decode_int4_empty_context_gets_zeros(pkv, orc):
     assert_close(got[[1, 3]], ref[[1, 3]], W.BF16, "int4 around empty contexts")
 
 
-def test_decode_int4_short_context_config_sampled(pkv, orc):
-    """Batch 512, lognormal contexts, block 16, 32/8 heads, shuffled 80000-block pool, in int4; the
-    oracle checks the shortest, the longest and a seeded draw of sequences."""
+def test_decode_int4_short_context_config(pkv, orc):
+    """Batch 512, lognormal contexts, block 16, 32/8 heads, shuffled 80000-block pool, in int4: every output
+    against the oracle."""
     c = W.make_config(3)
-    rng = np.random.default_rng(1004)
-    seqs = np.array(sorted({int(np.argmin(c.context_lens)), int(np.argmax(c.context_lens))} |
-                           set(rng.choice(c.num_seqs, 12, replace=False).tolist())), np.int32)
-    got, ref = run_int4_decode(pkv, orc, c, seqs=seqs)
-    assert_close(got[seqs], ref, W.BF16, "int4 config")
-    assert np.isfinite(got).all()
+    got, ref = run_int4_decode(pkv, orc, c)
+    assert_close(got, ref, W.BF16, "int4 config")
+    assert_rel_norm(got, ref, what="int4 config")
 
 
-def test_decode_int4_long_context_config_sampled(pkv, orc):
-    """Batch 16, contexts U[16k, 32k], block 256, 64/8 heads (every sequence split into parts): two sequences
-    against the oracle, every output finite."""
+def test_decode_int4_long_context_planted_keys(pkv, orc):
+    """Batch 16, contexts U[16k, 32k], block 256, 64/8 heads (every sequence split into parts) in int4, with two
+    dominant keys planted per query head at tile, block, part and sequence bounds (exact in int4: one magnitude
+    per row): every output against the oracle."""
     c = W.make_config(4)
-    seqs = np.array([int(np.argmin(c.context_lens)), int(np.argmax(c.context_lens))], np.int32)
-    got, ref = run_int4_decode(pkv, orc, c, seqs=seqs)
-    assert_close(got[seqs], ref, W.BF16, "int4 long contexts")
-    assert np.isfinite(got).all()
+    W.plant_dominant_keys(c, N.needle_positions(c, np.random.default_rng(47), decode_workers("q8")))
+    got, ref = run_int4_decode(pkv, orc, c)
+    assert_close(got, ref, W.BF16, "int4 long contexts, planted keys")
+    assert_rel_norm(got, ref, what="int4 long contexts, planted keys")
 
 
 def test_decode_int4_plan_run_equals_whole_call(pkv, orc):

@@ -5,8 +5,9 @@ import numpy as np
 import pytest
 import torch
 
+import needles as N
 import workloads as W
-from gpu_util import assert_close, device_pool, i32, oracle_decode_case, to_torch
+from gpu_util import assert_close, decode_workers, device_pool, i32, oracle_decode_case, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -108,3 +109,97 @@ def test_short_context_workload_plan_run(pkv):
                                workspace=torch.empty(n, dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
     assert torch.equal(out, whole)
+
+
+def _status(pkv, ws):
+    st = pkv.paged_attention_decode_status(ws)
+    torch.cuda.synchronize()
+    return int(st.item())
+
+
+def test_run_refuses_a_plan_for_other_sizes(pkv):
+    """A run over a workspace planned for other sizes (max_context_len, head count, cache kind, batch) writes
+    nothing and raises the workspace's run status; a plan for the right sizes clears it and the run then equals
+    the whole call. The workspace is zeroed and twice the larger size, the planned batch is the smaller one,
+    and a canary fills the second half, so the mismatched runs stay inside their buffers whatever they do."""
+    c = _case(60)
+    kc, vc = device_pool(c.pool)
+    pkv.kv_cache_store(to_torch(c.key, c.dtype), to_torch(c.value, c.dtype), kc, vc, i32(c.slot_mapping))
+    b, hq, hkv, d, bs = c.num_seqs, c.num_heads, c.num_kv_heads, c.head_dim, c.block_size
+    big_b = b + 3
+    need = max(pkv.decode_workspace_size(big_b, hq, hkv, d, bs, 2048), pkv.decode_workspace_size(b, hq, hkv, d, bs, 2048))
+    ws = torch.zeros(2 * need, dtype=torch.uint8, device="cuda")
+    ws[need:] = 0xA5
+    q = to_torch(c.query, c.dtype)
+    bt, cl = i32(c.block_tables), i32(c.context_lens)
+    q_big = torch.cat([q, q[:3]])
+    bt_big = torch.cat([bt, bt[:3]])
+    mlen = int(c.max_context_len)
+
+    def plan(max_len=mlen, heads=hq, cache="elements", lens=cl):
+        pkv.paged_attention_decode_plan(lens, max_len, heads, hkv, d, bs, ws, cache=cache)
+
+    cases = [
+        ("max_context_len", lambda: plan(max_len=mlen), lambda out: pkv.paged_attention_decode_run(
+            out, q, kc, vc, bt, 2048, c.scale, ws), q),
+        ("num_heads", lambda: plan(heads=hkv * 2), lambda out: pkv.paged_attention_decode_run(
+            out, q, kc, vc, bt, mlen, c.scale, ws), q),
+        ("cache kind", lambda: plan(cache="int8"), lambda out: pkv.paged_attention_decode_run(
+            out, q, kc, vc, bt, mlen, c.scale, ws), q),
+        ("num_seqs", lambda: plan(), lambda out: pkv.paged_attention_decode_run(
+            out, q_big, kc, vc, bt_big, mlen, c.scale, ws), q_big),
+    ]
+    for name, make_plan, run, qq in cases:
+        make_plan()
+        out = torch.full_like(qq, float("nan"))
+        run(out)
+        assert _status(pkv, ws) == 1, f"{name}: mismatch not flagged"
+        assert torch.isnan(out.float()).all(), f"{name}: a mismatched run wrote output"
+        assert bool((ws[need:] == 0xA5).all()), f"{name}: write past the workspace"
+    plan()
+    assert _status(pkv, ws) == 0
+    out = torch.full_like(q, float("nan"))
+    pkv.paged_attention_decode_run(out, q, kc, vc, bt, mlen, c.scale, ws)
+    whole = torch.full_like(q, float("nan"))
+    pkv.paged_attention_decode(whole, q, kc, vc, bt, cl, mlen, c.scale, workspace=torch.empty_like(ws))
+    torch.cuda.synchronize()
+    assert _status(pkv, ws) == 0
+    assert torch.equal(out, whole)
+
+
+PLAN_CASES = [("short-context workload", 3, "elements"), ("long-context workload", 4, "elements"),
+              ("batch-64 workload", 2, "elements"), ("short-context workload, int8 cache", 3, "int8"),
+              ("long-context workload, int4 cache", 4, "int4")]
+
+
+@pytest.mark.parametrize("name,cfg,cache", PLAN_CASES, ids=[p[0] for p in PLAN_CASES])
+def test_plan_matches_its_rule(pkv, name, cfg, cache):
+    """White-box check of the plan kernel's integer work: the work list it leaves in the workspace (control
+    word 0 = part count; 16-byte items {seq, first token, tokens, partial slot} from byte 256) holds exactly
+    the parts of the documented rule (restated on the host in tests/needles.py), longest first by its
+    64 length buckets, with one-part sequences writing directly (slot -1) and split sequences owning distinct
+    consecutive partial slots."""
+    c = W.make_config(cfg)
+    cl = i32(c.context_lens)
+    n = pkv.decode_workspace_size(c.num_seqs, c.num_heads, c.num_kv_heads, c.head_dim, c.block_size,
+                                  c.max_context_len)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    pkv.paged_attention_decode_plan(cl, c.max_context_len, c.num_heads, c.num_kv_heads, c.head_dim, c.block_size, ws,
+                                    cache=cache)
+    torch.cuda.synchronize()
+    words = ws.view(torch.int32).cpu().numpy()
+    nparts = int(words[0])
+    items = words[64:64 + 4 * nparts].reshape(nparts, 4)
+    want = N.plan_parts(c.context_lens, c.num_kv_heads, c.block_size,
+                        decode_workers("bf16" if cache == "elements" else "q8"))
+    assert sorted(map(tuple, items[:, :3].tolist())) == sorted(want)
+    maxlen = int(items[:, 2].max())
+    buckets = np.minimum(63, (maxlen - items[:, 2].astype(np.int64)) * 64 // maxlen)
+    assert np.all(np.diff(buckets) >= 0), "parts are not listed longest first"
+    for i in range(c.num_seqs):
+        mine = items[items[:, 0] == i]
+        if len(mine) == 1:
+            assert mine[0, 3] == -1
+        else:
+            slots = np.sort(mine[:, 3])
+            assert slots[0] >= 0 and np.array_equal(slots, np.arange(slots[0], slots[0] + len(mine)))

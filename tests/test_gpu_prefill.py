@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_util import assert_close, oracle_prefill_case, run_prefill_case
+from gpu_util import assert_close, assert_rel_norm, oracle_prefill_case, run_prefill_case
 
 pytestmark = pytest.mark.gpu
 
@@ -55,14 +55,11 @@ def test_remaining_groups(pkv, orc, group):
 @pytest.mark.parametrize("bs", [16, 64])
 def test_block_table_past_64_blocks(pkv, orc, bs):
     """Cached prefixes spanning more than 64 blocks (block ids past the first 64 come from the table in
-    memory, not from the lane-held slice): rows near the chunk's end and a sample."""
+    memory, not from the lane-held slice): every row."""
     c = _case(80 + bs, [64 * bs + 77, 5], [70, 40], 4, bs)
     got = run_prefill_case(pkv, c)
     assert np.isfinite(got).all()
-    rng = np.random.default_rng(81)
-    rows = np.array(sorted(set(range(c.total_q - 8, c.total_q)) | set(rng.choice(c.total_q, 24, replace=False).tolist())),
-                    np.int32)
-    assert_close(got[rows], oracle_prefill_case(orc, c, rows=rows), W.BF16, f"long table bs{bs}")
+    assert_close(got, oracle_prefill_case(orc, c), W.BF16, f"long table bs{bs}")
 
 
 @pytest.mark.parametrize("n", [64, 65, 130])
@@ -90,18 +87,15 @@ def test_empty_chunks_in_batch(pkv, orc):
     assert_close(got, oracle_prefill_case(orc, c), W.BF16, "empty chunks")
 
 
-def test_chunked_prefill_config_sampled(pkv, orc):
-    """32 sequences, prefix U[0, 2048] + chunk U[64, 512], block 256, 32/8 heads: every sequence's first
-    and last rows plus a seeded sample, all heads and dims; and every output finite."""
+def test_chunked_prefill_config(pkv, orc):
+    """32 sequences, prefix U[0, 2048] + chunk U[64, 512], block 256, 32/8 heads: every row, head and dim
+    against the oracle, plus the relative error norm."""
     c = W.chunked_prefill()
     got = run_prefill_case(pkv, c)
     assert np.isfinite(got).all()
-    rng = np.random.default_rng(55)
-    rows = set(c.cu_seqlens_q[:-1].tolist()) | set((c.cu_seqlens_q[1:] - 1).tolist())
-    rows |= set(rng.choice(c.total_q, size=256, replace=False).tolist())
-    rows = np.array(sorted(rows), np.int32)
-    ref = oracle_prefill_case(orc, c, rows=rows)
-    assert_close(got[rows], ref, W.BF16, "chunked prefill config")
+    ref = oracle_prefill_case(orc, c)
+    assert_close(got, ref, W.BF16, "chunked prefill config")
+    assert_rel_norm(got, ref, what="chunked prefill config")
 
 
 def test_prefill_last_row_matches_decode(pkv, orc):

@@ -101,17 +101,13 @@ def test_prefill_q8_non_causal(pkv, orc, kind):
 
 
 @pytest.mark.parametrize("kind", ["int8", "fp8"])
-def test_prefill_q8_chunked_config_sampled(pkv, orc, kind):
+def test_prefill_q8_chunked_config(pkv, orc, kind):
     """The chunked-prefill workload (32 sequences, prefix U[0, 2048] + chunk U[64, 512], block 256, 32/8 heads)
-    over an 8-bit cache: every sequence's first and last rows plus a seeded sample; every output finite."""
+    over an 8-bit cache: every row, head and dim against the oracle."""
     c = W.chunked_prefill()
-    rng = np.random.default_rng(56)
-    rows = set(c.cu_seqlens_q[:-1].tolist()) | set((c.cu_seqlens_q[1:] - 1).tolist())
-    rows |= set(rng.choice(c.total_q, size=96, replace=False).tolist())
-    rows = np.array(sorted(rows), np.int32)
-    got, ref = run_q8_prefill(pkv, orc, kind, c, rows=rows)
+    got, ref = run_q8_prefill(pkv, orc, kind, c)
     assert np.isfinite(got).all()
-    assert_close(got[rows], ref, W.BF16, f"{kind} chunked prefill config")
+    assert_close(got, ref, W.BF16, f"{kind} chunked prefill config")
 
 
 @pytest.mark.parametrize("kind", ["int8", "fp8"])

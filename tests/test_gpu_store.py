@@ -52,7 +52,7 @@ def test_store_empty_and_all_padding(pkv, orc):
                        torch.empty(0, dtype=torch.int32, device="cuda"))
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 5], ids=lambda n: W.CONFIGS[n].__name__)
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5], ids=lambda n: W.CONFIGS[n].__name__)
 def test_store_bit_exact_configs(pkv, orc, cfg):
     """The store step of each benchmark workload (one token per sequence; the whole chunk for prefill) at full
     size."""
@@ -66,7 +66,7 @@ def test_store_bit_exact_configs(pkv, orc, cfg):
     assert np.array_equal(to_storage(vc, c.dtype).view(np.uint8), vc_h.view(np.uint8))
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5], ids=lambda n: W.CONFIGS[n].__name__)
 def test_gather_bit_exact(pkv, orc, cfg):
     """Gather of every sequence after the store equals the oracle's gather, byte for byte."""
     c = W.make_config(cfg)

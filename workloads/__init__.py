@@ -329,6 +329,61 @@ def make_prefill_case(name, seed, dtype, prefix_lens, chunk_lens, num_heads, num
                        num_blocks, scale, bool(causal), p, c, cu_q, cu_k, bt, slots, q, kn, vn, pool)
 
 
+def plant_dominant_keys(case: DecodeCase, positions, gap: float = 36.0) -> DecodeCase:
+    """Make chosen cached tokens dominate each query head's softmax (in place; returns the case).
+
+    ``positions[i][h]`` lists the logical tokens of sequence ``i`` planted for query head ``h`` (kv head
+    ``h // G``, G = Hq / Hkv); the positions of the heads of one kv head must be distinct. The head dims are
+    split into G disjoint runs of D / G: head ``h`` keeps its drawn query values on run ``h % G`` and gets zeros
+    elsewhere, and each planted token's key row (for kv head ``h // G``) is ``c * sign(q_h)`` on that run and
+    zero elsewhere. So a planted key scores ``scale * c * sum|q_h|`` for its own head and exactly 0 for the other
+    heads of its group, while an ordinary N(0, 1) key scores about N(0, (scale |q_h|)^2). ``c`` (rounded to
+    bf16, the same for all of a head's planted keys, so their scores are equal) puts the planted score
+    ``gap + 6 scale |q_h|`` above zero: every other token of the head then carries a weight below e^-gap
+    relative to a planted one. All non-zero elements of a planted row have one magnitude, so an int8, fp8 or
+    int4 cache represents the row exactly. Values are left as drawn.
+    A position ``context_lens[i] - 1`` (the token stored this step) is planted in ``case.key``."""
+    hq, hkv, d, bs = case.num_heads, case.num_kv_heads, case.head_dim, case.block_size
+    g = hq // hkv
+    run = d // g
+    q = to_f32(case.query, case.dtype).astype(np.float64)
+    blk_index = {int(b): k for k, b in enumerate(case.pool.used_blocks)}
+    as_storage = (lambda a: f32_to_bf16_bits(np.asarray(a, np.float32))) if case.dtype == BF16 else \
+        (lambda a: np.asarray(a, np.float32))
+    for i, per_head in enumerate(positions):
+        n = int(case.context_lens[i])
+        taken = {}
+        for h, pos in enumerate(per_head):
+            if len(pos) == 0:
+                continue
+            lo, hi = (h % g) * run, (h % g + 1) * run
+            qh = q[i, h].copy()
+            qh[:lo] = 0.0
+            qh[hi:] = 0.0
+            sgn = np.where(qh[lo:hi] < 0, -1.0, 1.0)
+            l1, l2 = np.abs(qh[lo:hi]).sum(), math.sqrt((qh[lo:hi] ** 2).sum())
+            if l1 == 0.0:                                   # no usable query: give the head a unit entry
+                qh[lo], l1, l2 = 1.0, 1.0, 1.0
+            c32 = np.array([(gap + 6 * case.scale * l2) / (case.scale * l1)], np.float32)
+            c = float(to_f32(as_storage(c32), case.dtype)[0])      # rounded to the storage dtype
+            case.query[i, h] = as_storage(qh.astype(np.float32))
+            row = np.zeros(d, np.float32)
+            row[lo:hi] = c * sgn
+            kvh = h // g
+            for t in pos:
+                t = int(t)
+                if not 0 <= t < n:
+                    raise ValueError(f"position {t} outside sequence {i} of {n} tokens")
+                if taken.setdefault((kvh, t), h) != h:
+                    raise ValueError(f"position {t} of sequence {i} planted for two heads of kv head {kvh}")
+                if t == n - 1:
+                    case.key[i, kvh] = as_storage(row)
+                else:
+                    k = blk_index[int(case.block_tables[i, t // bs])]
+                    case.pool.key_blocks[k, kvh, t % bs] = as_storage(row)
+    return case
+
+
 # ---- the five workloads -------------------------------------------------------------------------
 
 def lognormal_lengths(rng, n, median, sigma, lo, hi):
