@@ -2,6 +2,8 @@
 // The declarations, argument meanings and error rules are in include/pagedkv.h.
 #include <math.h>
 #include <stdarg.h>
+
+#include <atomic>
 #include <stdio.h>
 #include <string.h>
 
@@ -95,15 +97,20 @@ constexpr int DECODE_MAX_WORKERS = 256 * DECODE_WAVES_PER_CU;
 constexpr int DECODE_MIN_STRATA = PKV_DECODE_MIN_STRATA;
 constexpr int DECODE_MIN_PART_TILES = 4;
 
+// Per-device cache of the worker count. Any host thread may call in: the entries are atomics, and two
+// threads that both miss compute and store the same value.
 int decode_workers() {
-    static int cached[64];
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return DECODE_MAX_WORKERS;
-    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    if (dev < 64) {
+        const int w = cached[dev].load(std::memory_order_relaxed);
+        if (w > 0) return w;
+    }
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
     const int w = cus * DECODE_WAVES_PER_CU < DECODE_MAX_WORKERS ? cus * DECODE_WAVES_PER_CU : DECODE_MAX_WORKERS;
-    if (dev < 64) cached[dev] = w;
+    if (dev < 64) cached[dev].store(w, std::memory_order_relaxed);
     return w;
 }
 
