@@ -377,6 +377,26 @@ pkv_status pkv_paged_attention_decode_int4_run(pkv_dtype dtype, void *out, const
  */
 pkv_status pkv_paged_attention_decode_status(const void *workspace, int32_t *status, hipStream_t stream);
 
+/*
+ * paged_attention_decode_noalloc: pkv_paged_attention_decode with no workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the call allocates nothing and takes no workspace; it uses a library-owned scratch array of
+ * PKV_NOALLOC_SCRATCH_BYTES per GPU, created when the library's code loads on that GPU and held until the
+ * process ends. Sizes whose workspace bound (pkv_paged_attention_decode_workspace_size) exceeds it are refused
+ * with PKV_EWORKSPACE before anything is launched; other arguments, errors and results are those of
+ * pkv_paged_attention_decode (bit-identical outputs). Every call on one GPU uses the same array and leaves
+ * its contents there: calls that may overlap on one GPU (different streams, or host threads without an
+ * order between their calls) race; keep them on one stream. Nothing in it needs to start at zero: each
+ * call's plan kernel writes the work list and control words its decode and reduce kernels read.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pkv_status pkv_paged_attention_decode_noalloc(pkv_dtype dtype, void *out, const void *query, const void *key_cache,
+                                              const void *value_cache, const int32_t *block_tables,
+                                              int32_t block_table_stride, const int32_t *context_lens,
+                                              int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                              int64_t num_blocks, float scale, hipStream_t stream);
+
 /* Message of the calling thread's last non-OK status ("" if none). Owned by the library. */
 const char *pkv_last_error(void);
 

@@ -45,6 +45,8 @@ def load_library(path: str = LIB_PATH):
         "pkv_kv_cache_gather": [ctypes.c_int, P, P, P, P, P, I32, I32, I32, I32, I64, P],
         "pkv_paged_attention_decode": [ctypes.c_int, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32, I64, F, P,
                                        SZ, P],
+        "pkv_paged_attention_decode_noalloc": [ctypes.c_int, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32,
+                                               I64, F, P],
         "pkv_paged_attention_prefill": [ctypes.c_int, P, P, P, P, P, I32, P, P, I32, I32, I32, I32, I32, I32, I32,
                                         I64, F, I32, P],
         "pkv_kv_cache_store_int8": [ctypes.c_int, P, P, P, P, P, P, P, I64, I32, I32, I32, I64, P],
@@ -215,6 +217,27 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
 
 
 _CACHE_KINDS = {"elements": 0, "int8": 1, "fp8": 2, "int4": 3}
+
+
+def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len,
+                                   scale, stream=None):
+    """``paged_attention_decode`` without a workspace: the library's per-GPU scratch array stands in for it
+    (nothing is allocated). Sizes past the scratch raise ``PagedKVError`` (PKV_EWORKSPACE); calls that may
+    overlap on one GPU race on the shared array."""
+    lib = load_library()
+    _dev(out, query, key_cache, value_cache, block_tables, context_lens)
+    _i32(block_tables, context_lens)
+    b, hq, d = query.shape
+    nb, hkv, bs, d2 = key_cache.shape
+    if out.shape != query.shape or out.dtype != query.dtype or d2 != d or value_cache.shape != key_cache.shape:
+        raise ValueError("shape mismatch between out, query and the caches")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or context_lens.shape != (b,):
+        raise ValueError("block_tables must be [B, stride] and context_lens [B]")
+    _check(lib.pkv_paged_attention_decode_noalloc(_dtype_code(query), _ptr(out), _ptr(query), _ptr(key_cache),
+                                                  _ptr(value_cache), _ptr(block_tables), block_tables.shape[1],
+                                                  _ptr(context_lens), b, int(max_context_len), hq, hkv, d, bs, nb,
+                                                  float(scale), _stream(stream)))
+    return out
 
 
 def paged_attention_decode_plan(context_lens, max_context_len, num_heads, num_kv_heads, head_dim, block_size,

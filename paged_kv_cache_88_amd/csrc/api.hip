@@ -4,6 +4,7 @@
 #include <stdarg.h>
 
 #include <atomic>
+#include <mutex>
 #include <stdio.h>
 #include <string.h>
 
@@ -503,6 +504,72 @@ pkv_status pkv_paged_attention_decode_int4_run(pkv_dtype dtype, void *out, const
                      key_scale, value_scale, block_tables, block_table_stride, nullptr, num_seqs, max_context_len,
                      num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, workspace, workspace_bytes,
                      stream, DECODE_RUN_ONLY);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of the no-allocation decode: one array per GPU in the library's code object, held until the process
+// ends. Host code reaches it only through the device address looked up below, once per device with that
+// device current, never through the array's name (a host-side stand-in).
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::atomic<void *> g_scratch_ptr[SCRATCH_MAX_DEVICES];
+std::mutex g_scratch_mu;
+
+pkv_status scratch_on_current_device(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    REQUIRE(dev >= 0 && dev < SCRATCH_MAX_DEVICES, PKV_EUNSUPPORTED, "device %d: the no-allocation decode serves "
+            "devices 0..%d", dev, SCRATCH_MAX_DEVICES - 1);
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+            REQUIRE(p != nullptr && ((uintptr_t)p & 255u) == 0, PKV_EHIP, "scratch address %p unusable", p);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attention_decode_noalloc(pkv_dtype dtype, void *out, const void *query, const void *key_cache,
+                                              const void *value_cache, const int32_t *block_tables,
+                                              int32_t block_table_stride, const int32_t *context_lens,
+                                              int32_t num_seqs, int32_t max_context_len, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                              int64_t num_blocks, float scale, hipStream_t stream) {
+    const size_t need = pkv_paged_attention_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                                  block_size, max_context_len);
+    REQUIRE(need <= PKV_NOALLOC_SCRATCH_BYTES, PKV_EWORKSPACE,
+            "these sizes need %zu bytes of decode workspace; the no-allocation decode holds %zu (use "
+            "pkv_paged_attention_decode with a caller workspace)", need, (size_t)PKV_NOALLOC_SCRATCH_BYTES);
+    // every host-side check first, against a stand-in address that nothing dereferences
+    pkv::DecodeArgs a{};
+    pkv_status st = decode_args(a, dtype, out, query, key_cache, value_cache, block_tables, block_table_stride,
+                                context_lens, num_seqs, max_context_len, num_heads, num_kv_heads, head_dim,
+                                block_size, num_blocks, scale, (void *)(uintptr_t)256, PKV_NOALLOC_SCRATCH_BYTES);
+    if (st != PKV_OK || num_seqs == 0) return st;
+    void *ws = nullptr;
+    st = scratch_on_current_device(&ws);
+    if (st != PKV_OK) return st;
+    st = decode_args(a, dtype, out, query, key_cache, value_cache, block_tables, block_table_stride, context_lens,
+                     num_seqs, max_context_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, ws,
+                     PKV_NOALLOC_SCRATCH_BYTES);
+    if (st != PKV_OK) return st;
+    return hip_status(pkv::launch_decode(a, dtype == PKV_BF16, head_dim, num_heads / num_kv_heads, stream),
+                      "paged_attention_decode_noalloc launch");
 }
 
 pkv_status pkv_paged_attention_decode_status(const void *workspace, int32_t *status, hipStream_t stream) {

@@ -173,6 +173,19 @@ def test_decode_status_validation(lib):
     assert "256-byte" in _err(lib)
 
 
+def test_decode_noalloc_validation(lib):
+    """The no-allocation decode refuses, before any HIP call, sizes whose workspace bound passes its scratch
+    and the arguments the workspace call refuses."""
+    f = lib.pkv_paged_attention_decode_noalloc
+    # (dtype, out, q, kc, vc, bt, stride, context_lens, B, max_len, Hq, Hkv, D, bs, NB, scale, stream)
+    assert f(1, FAKE, FAKE, FAKE, FAKE, FAKE, 512, FAKE, 1024, 8192, 32, 8, 128, 16, 64, 0.1, None) == 3
+    assert "no-allocation" in _err(lib)
+    assert f(1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 8, 2, 96, 16, 64, 0.1, None) == 2      # head_dim
+    assert f(1, None, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 8, 2, 128, 16, 64, 0.1, None) == 1     # null out
+    assert f(1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 65, 8, 2, 128, 16, 64, 0.1, None) == 1     # past table
+    assert f(1, None, None, None, None, None, 4, None, 0, 64, 8, 2, 128, 16, 64, 0.1, None) == 0     # no-op
+
+
 def test_binding_fails_loudly_without_library(pkv, tmp_path):
     saved = pkv._lib
     try:
