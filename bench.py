@@ -14,7 +14,10 @@ over the timed steps), plus the roofline of the decode call measured with HIP ev
 stream (recorded around every fourth decode call of the timed steps: each event costs the stream
 about 5 us, so recording them around every call would slow the steps it measures), and the CPU oracle's rate
 on a bounded sample of the same workload. Secondary legs (not part of `value`): the same decode over
-an int8 and over an fp8 (E4M3) cache, and the chunked-prefill workload on MFMA.
+int8, fp8 (E4M3) and int4 caches; the decode call on the other two decode workloads (batch 64 at block 256,
+batch 16 at 16k-32k tokens); the chunked-prefill workload on MFMA (bf16, int8 and fp8 caches); and the
+practical ceilings measured on the same GPU: the decode's read pattern (scrambled 4 KB and 64 KB chunks), the
+matrix cores' rate for the prefill's MFMA instruction, and a bf16 GEMM.
 """
 from __future__ import annotations
 
@@ -198,6 +201,119 @@ def cpu_baseline(c, target_s=12.0, single_s=3.0):
                                       f"tokens) x {reps1} passes, float64, {dt1:.2f} s"}}
 
 
+def bench_ceilings(pkv, torch, dev, reps=10):
+    """Practical ceilings on this GPU, measured with HIP events on one stream around `reps` back-to-back launches:
+    * the decode's read pattern (include/pagedkv_measure.h): a buffer read once as 4 KB chunks (the (block, kv
+      head) slab at block size 16) and as 64 KB chunks (block size 256) in scrambled order; the best over 1 GiB
+      and 8 GiB buffers and 4, 8 and 16 waves per compute unit (the rate moves by a few percent with the buffer's
+      size and place; the best is the hardest bar);
+    * the matrix cores' rate for v_mfma_f32_16x16x32_bf16 (the prefill's instruction) on register operands,
+      best of 4 and 8 waves per compute unit;
+    * a bf16 GEMM through torch.matmul (the vendor BLAS), 8192^3."""
+    stream = torch.cuda.current_stream()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(4096 * cus * 8, dtype=torch.uint8, device=dev)
+
+    def timed(launch):
+        for _ in range(3):
+            launch()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            launch()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    read = {}
+    for gib in (1, 8):
+        buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+        buf.fill_(0x3c)
+        for chunk in (4096, 65536):
+            key = f"chunks_{chunk // 1024}k"
+            for wpc in (4, 8, 16):
+                nbytes = pkv.measure_read_chunks(buf, chunk, wpc, sink, stream=stream)
+                ms = timed(lambda: pkv.measure_read_chunks(buf, chunk, wpc, sink, stream=stream))
+                gbs = nbytes / (ms * 1e-3) / 1e9
+                if key not in read or gbs > read[key]["gbs"]:
+                    read[key] = {"gbs": round(gbs, 1), "buffer_gib": gib, "waves_per_cu": wpc, "ms": round(ms, 5),
+                                 "bytes": nbytes, "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del buf
+        torch.cuda.empty_cache()
+    mfma = None
+    for wpc in (4, 8):
+        fl = pkv.measure_mfma_rate(20000, wpc, sink, stream=stream)
+        ms = timed(lambda: pkv.measure_mfma_rate(20000, wpc, sink, stream=stream))
+        tf = fl / (ms * 1e-3) / 1e12
+        if mfma is None or tf > mfma["tflops"]:
+            mfma = {"tflops": round(tf, 1), "waves_per_cu": wpc, "frac_of_peak": round(tf * 1e12 / MFMA_BF16_PEAK, 4),
+                    "instruction": "v_mfma_f32_16x16x32_bf16, 8 independent chains per wave, register operands"}
+    n = 8192
+    a = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    b = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda: torch.matmul(a, b, out=c))
+    gemm = {"tflops": round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1), "shape": f"{n}x{n}x{n} bf16 torch.matmul",
+            "frac_of_peak": round(2 * n ** 3 / (ms * 1e-3) / MFMA_BF16_PEAK, 4)}
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"read_pattern": read, "mfma_16x16x32_bf16": mfma, "bf16_gemm": gemm}
+
+
+def bench_decode_workload(pkv, torch, W, cfg, dev, steps, warmup):
+    """The decode call alone on another decode workload (pool copies rotated so K/V come from HBM): HIP
+    events around every call."""
+    c = W.make_config(cfg)
+
+    def tt(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    nbytes = decode_bytes(c)
+    copies = max(2, min(8, int(np.ceil(2.0e9 / nbytes))))
+    shape = (c.num_blocks,) + c.pool.block_shape
+    idx = torch.from_numpy(c.pool.used_blocks.astype(np.int64)).to(dev)
+    kb, vb = tt(c.pool.key_blocks), tt(c.pool.value_blocks)
+    kn, vn, sm = tt(c.key), tt(c.value), torch.from_numpy(c.slot_mapping).to(dev)
+    pools = []
+    for _ in range(copies):
+        kc = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+        vc = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+        kc.index_copy_(0, idx, kb)
+        vc.index_copy_(0, idx, vb)
+        pkv.kv_cache_store(kn, vn, kc, vc, sm)
+        pools.append((kc, vc))
+    del kb, vb
+    q = tt(c.query)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(c.block_tables).to(dev)
+    cl = torch.from_numpy(c.context_lens).to(dev)
+    ws = torch.empty(pkv.decode_workspace_size(c.num_seqs, c.num_heads, c.num_kv_heads, c.head_dim, c.block_size,
+                                               c.max_context_len), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for k in range(warmup + steps):
+        kc, vc = pools[k % copies]
+        if k >= warmup:
+            ev[k - warmup][0].record(stream)
+        pkv.paged_attention_decode(out, q, kc, vc, bt, cl, c.max_context_len, c.scale, workspace=ws, stream=stream)
+        if k >= warmup:
+            ev[k - warmup][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    gbs = nbytes / (ms.mean() * 1e-3) / 1e9
+    res = {"workload": c.name, "num_seqs": c.num_seqs, "sum_context_tokens": int(c.context_lens.sum()),
+           "block_size": c.block_size, "num_heads": c.num_heads, "num_kv_heads": c.num_kv_heads,
+           "decode_ms": {"mean": round(float(ms.mean()), 5), "median": round(float(np.median(ms)), 5),
+                         "p10": round(float(np.percentile(ms, 10)), 5), "p90": round(float(np.percentile(ms, 90)), 5)},
+           "algorithmic_bytes": nbytes, "achieved_gbs": round(gbs, 1),
+           "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "decode_tokens_per_s": round(c.num_seqs / (ms.mean() * 1e-3), 1), "pool_copies_rotated": copies,
+           "outputs_finite": bool(torch.isfinite(out.float()).all().item())}
+    del pools
+    torch.cuda.empty_cache()
+    return res
+
+
 def prefill_flops(c) -> int:
     """Algorithmic flops of one causal chunked-prefill call: 2 flops per multiply-add of QK^T and of PV over
     the visible (query, key) pairs only; softmax not counted."""
@@ -207,9 +323,11 @@ def prefill_flops(c) -> int:
     return 4 * c.head_dim * c.num_heads * pairs
 
 
-def bench_prefill(pkv, torch, dev, iters=20):
+def bench_prefill(pkv, torch, dev, iters=20, copies=3):
     """Chunked prefill (32 sequences, prefix U[0, 2048] + chunk U[64, 512], block 256, 32/8 heads, bf16):
-    store of the chunk then causal prefill, timed with HIP events on the launch stream."""
+    store of the chunk then causal prefill, timed with HIP events on the launch stream. Successive calls read
+    different copies of the pool (the K/V a call reads, ~0.3 GB, would otherwise partly stay in the last-level
+    cache)."""
     import workloads as W
 
     c = W.chunked_prefill()
@@ -219,10 +337,15 @@ def bench_prefill(pkv, torch, dev, iters=20):
 
     shape = (c.num_blocks,) + c.pool.block_shape
     idx = torch.from_numpy(c.pool.used_blocks.astype(np.int64)).to(dev)
-    kc = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
-    vc = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
-    kc.index_copy_(0, idx, tt(c.pool.key_blocks))
-    vc.index_copy_(0, idx, tt(c.pool.value_blocks))
+    kb, vb = tt(c.pool.key_blocks), tt(c.pool.value_blocks)
+    pools = []
+    for _ in range(copies):
+        kc = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+        vc = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+        kc.index_copy_(0, idx, kb)
+        vc.index_copy_(0, idx, vb)
+        pools.append((kc, vc))
+    del kb, vb
     q, kn, vn = tt(c.query), tt(c.key), tt(c.value)
     out = torch.empty_like(q)
     bt = torch.from_numpy(c.block_tables).to(dev)
@@ -233,6 +356,7 @@ def bench_prefill(pkv, torch, dev, iters=20):
            torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     for k in range(iters + 3):
         e = ev[k - 3] if k >= 3 else None
+        kc, vc = pools[k % copies]
         if e:
             e[0].record(stream)
         pkv.kv_cache_store(kn, vn, kc, vc, sm, stream=stream)
@@ -249,23 +373,29 @@ def bench_prefill(pkv, torch, dev, iters=20):
     res = {"workload": c.name, "total_q": c.total_q, "prefill_ms": round(pf_ms, 5), "store_ms": round(st_ms, 5),
            "gflop": round(fl / 1e9, 2), "tflops": round(fl / (pf_ms * 1e-3) / 1e12, 2),
            "mfma_utilization": round(fl / (pf_ms * 1e-3) / MFMA_BF16_PEAK, 4), "peak_tflops": MFMA_BF16_PEAK / 1e12,
-           "store_gbs": round(store_bytes(c) / (st_ms * 1e-3) / 1e9, 1),
+           "store_gbs": round(store_bytes(c) / (st_ms * 1e-3) / 1e9, 1), "pool_copies_rotated": copies,
            "outputs_finite": bool(torch.isfinite(out.float()).all().item())}
+    del pools
+    torch.cuda.empty_cache()
     # the same prefill over 8-bit caches (every cached row and the chunk quantized by the 8-bit store)
     kr, vr, slots = W.cached_rows(c.pool)
     for kind in ("int8", "fp8"):
         code = torch.int8 if kind == "int8" else torch.uint8
-        kq = torch.zeros(shape, dtype=code, device=dev)
-        vq = torch.zeros(shape, dtype=code, device=dev)
-        ks = torch.zeros(shape[:3], dtype=torch.float32, device=dev)
-        vs = torch.zeros(shape[:3], dtype=torch.float32, device=dev)
         store = pkv.kv_cache_store_int8 if kind == "int8" else pkv.kv_cache_store_fp8
         prefill = pkv.paged_attention_prefill_int8 if kind == "int8" else pkv.paged_attention_prefill_fp8
-        store(tt(kr), tt(vr), kq, vq, ks, vs, torch.from_numpy(slots).to(dev), stream=stream)
-        store(kn, vn, kq, vq, ks, vs, sm, stream=stream)
+        qpools = []
+        for _ in range(copies):
+            kq = torch.zeros(shape, dtype=code, device=dev)
+            vq = torch.zeros(shape, dtype=code, device=dev)
+            ks = torch.zeros(shape[:3], dtype=torch.float32, device=dev)
+            vs = torch.zeros(shape[:3], dtype=torch.float32, device=dev)
+            store(tt(kr), tt(vr), kq, vq, ks, vs, torch.from_numpy(slots).to(dev), stream=stream)
+            store(kn, vn, kq, vq, ks, vs, sm, stream=stream)
+            qpools.append((kq, vq, ks, vs))
         ev8 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
         for k in range(iters + 3):
             e = ev8[k - 3] if k >= 3 else None
+            kq, vq, ks, vs = qpools[k % copies]
             if e:
                 e[0].record(stream)
             prefill(out, q, kq, vq, ks, vs, bt, cq, ck, c.max_seqlen_q, c.max_seqlen_k, c.scale, causal=True,
@@ -277,7 +407,8 @@ def bench_prefill(pkv, torch, dev, iters=20):
         res[f"{kind}_cache"] = {"prefill_ms": round(ms8, 5), "tflops": round(fl / (ms8 * 1e-3) / 1e12, 2),
                                 "mfma_utilization": round(fl / (ms8 * 1e-3) / MFMA_BF16_PEAK, 4),
                                 "outputs_finite": bool(torch.isfinite(out.float()).all().item())}
-        del kq, vq, ks, vs
+        del kq, vq, ks, vs, qpools
+        torch.cuda.empty_cache()
     return res
 
 
@@ -292,6 +423,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
     ap.add_argument("--no-int8", action="store_true", help="skip the quantized-cache (int8, fp8, int4) decode legs")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the read-pattern and MFMA ceiling legs")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the decode legs of the other two decode workloads")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -454,9 +588,28 @@ def main():
             leg = bench_q8(kind, pkv, torch, W, c, dev, copies, args.steps, args.warmup)
             leg["speedup_vs_bf16_cache"] = round(dec_avg_ms / leg["decode_ms"], 3)
             result[f"{kind}_cache"] = leg
+    pools = None
+    torch.cuda.empty_cache()
+    if not args.no_other_workloads:
+        result["other_workloads"] = {
+            W.CONFIGS[k].__name__: bench_decode_workload(pkv, torch, W, k, dev, max(args.steps, 20), args.warmup)
+            for k in (2, 3, 4) if k != args.config}
     if not args.no_prefill:
-        pools = None
         result["prefill"] = bench_prefill(pkv, torch, dev)
+    if not args.no_ceilings:
+        ceil = bench_ceilings(pkv, torch, dev)
+        result["ceilings"] = ceil
+        chunk = "chunks_4k" if c.block_size * c.head_dim * (2 if c.dtype == "bf16" else 4) <= 8192 else "chunks_64k"
+        rc = ceil["read_pattern"][chunk]["gbs"]
+        result["roofline"]["ceiling"] = {"measured_gbs": rc, "pattern": f"scrambled {chunk[7:]} chunks",
+                                         "frac_of_ceiling": round(achieved / rc, 4)}
+        for leg in result.get("other_workloads", {}).values():
+            lc = "chunks_4k" if leg["block_size"] <= 16 else "chunks_64k"
+            leg["frac_of_read_ceiling"] = round(leg["achieved_gbs"] / ceil["read_pattern"][lc]["gbs"], 4)
+        if "prefill" in result:
+            pf = result["prefill"]
+            pf["frac_of_mfma_rate"] = round(pf["tflops"] / ceil["mfma_16x16x32_bf16"]["tflops"], 4)
+            pf["frac_of_bf16_gemm"] = round(pf["tflops"] / ceil["bf16_gemm"]["tflops"], 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(c)
         result["cpu_baseline"]["host"] = platform.processor() or platform.machine()

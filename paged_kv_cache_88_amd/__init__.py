@@ -94,6 +94,12 @@ def load_library(path: str = LIB_PATH):
                  "pkv_bm_block_table", "pkv_bm_slot_mapping", "pkv_bm_take_copies", "pkv_bm_usage"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pkv_bm_last_error.restype = ctypes.c_char_p
+    lib.pkv_measure_read_chunks.argtypes = [P, SZ, I32, I32, P, SZ, P]
+    lib.pkv_measure_read_chunks.restype = ctypes.c_int
+    lib.pkv_measure_read_chunks_bytes.argtypes = [SZ, I32]
+    lib.pkv_measure_read_chunks_bytes.restype = I64
+    lib.pkv_measure_mfma_rate.argtypes = [I32, I32, P, SZ, ctypes.POINTER(ctypes.c_double), P]
+    lib.pkv_measure_mfma_rate.restype = ctypes.c_int
     lib.pkv_paged_attention_decode_status.argtypes = [P, P, P]
     lib.pkv_paged_attention_decode_status.restype = ctypes.c_int
     lib.pkv_paged_attention_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32]
@@ -294,6 +300,28 @@ def paged_attention_decode_status(workspace, status=None, stream=None):
     _dev(status)
     _check(load_library().pkv_paged_attention_decode_status(_ptr(workspace), _ptr(status), _stream(stream)))
     return status
+
+
+def measure_read_chunks(buffer, chunk_bytes, waves_per_cu, sink, stream=None) -> int:
+    """Enqueue one read of ``buffer`` (uint8, device) as scrambled chunks of ``chunk_bytes`` (the decode's
+    access pattern, include/pagedkv_measure.h); returns the bytes it reads."""
+    lib = load_library()
+    _dev(buffer, sink)
+    n = buffer.numel() * buffer.element_size()
+    _check(lib.pkv_measure_read_chunks(_ptr(buffer), n, int(chunk_bytes), int(waves_per_cu), _ptr(sink),
+                                       sink.numel() * sink.element_size(), _stream(stream)))
+    return int(lib.pkv_measure_read_chunks_bytes(n, int(chunk_bytes)))
+
+
+def measure_mfma_rate(iters, waves_per_cu, sink, stream=None) -> float:
+    """Enqueue independent v_mfma_f32_16x16x32_bf16 chains on every wave (include/pagedkv_measure.h);
+    returns the flops of the launch."""
+    lib = load_library()
+    _dev(sink)
+    fl = ctypes.c_double(0.0)
+    _check(lib.pkv_measure_mfma_rate(int(iters), int(waves_per_cu), _ptr(sink), sink.numel() * sink.element_size(),
+                                     ctypes.byref(fl), _stream(stream)))
+    return float(fl.value)
 
 
 def _cache_dims(kind, key_cache):

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libpagedkv.so")
-SOURCES = ["api.hip", "store.hip", "decode.hip", "prefill.hip", "block_manager.cpp"]
+SOURCES = ["api.hip", "store.hip", "decode.hip", "prefill.hip", "measure.hip", "block_manager.cpp"]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are disabled for the device code: hipcc would otherwise form them from
@@ -21,7 +21,10 @@ HIPCC_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
 
 # prefill: softmax maxima over MFMA results need no NaN quieting (masked scores are -inf, never NaN),
 # so IEEE mode is off there and fmax is a single v_max_f32.
-FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+# measure: MFMA accumulators in VGPRs; the default form there keeps them in AGPRs and copies every chain
+# through VGPRs on each loop turn, which would understate the matrix cores' issue rate.
+FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+              "measure.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:

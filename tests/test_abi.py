@@ -1,6 +1,7 @@
 """The C-ABI library on the CPU: it loads, exports every symbol include/pagedkv.h declares, and its
 host-side argument checks reject bad calls before any GPU work (no kernel is launched here)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -8,12 +9,16 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
-def declared_symbols():
-    text = open(HEADER, encoding="utf-8").read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+def declared_symbols(paths=(HEADER,)):
+    found = set()
+    for path in paths:
+        text = open(path, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        found |= set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text))
+    return sorted(found)
 
 
 @pytest.fixture(scope="module")
@@ -37,8 +42,25 @@ def test_header_declares_entry_points():
 
 
 def test_library_exports_every_declared_symbol(lib):
-    for name in declared_symbols():
+    """Every function any header under include/ declares (the paged cache, the block manager, the
+    measurement kernels) is exported."""
+    names = declared_symbols(HEADERS)
+    assert "pkv_bm_create" in names and "pkv_measure_read_chunks" in names
+    for name in names:
         assert hasattr(lib, name), name
+
+
+def test_measure_validation(lib):
+    """The measurement calls refuse bad arguments before any HIP call."""
+    sz = ctypes.c_size_t
+    f = lib.pkv_measure_read_chunks
+    f.argtypes = [ctypes.c_void_p, sz, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, sz, ctypes.c_void_p]
+    assert f(FAKE, 1 << 30, 3000, 8, FAKE, 1 << 24, None) == 1        # chunk not a power of two
+    assert f(FAKE, 1 << 30, 4096, 6, FAKE, 1 << 24, None) == 1        # waves per CU not a multiple of 4
+    assert f(None, 1 << 30, 4096, 8, FAKE, 1 << 24, None) == 1
+    g = lib.pkv_measure_read_chunks_bytes
+    g.argtypes, g.restype = [sz, ctypes.c_int32], ctypes.c_int64
+    assert g((1 << 30) + 5000, 4096) == 1 << 30 and g(3 * 4096, 4096) == 2 * 4096 and g(100, 4096) == 0
 
 
 def test_version(pkv):
