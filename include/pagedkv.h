@@ -16,7 +16,10 @@
  *                               store and decode over an int4 cache (two codes per byte);
  *   pkv_paged_attention_decode_plan and pkv_paged_attention_decode_run (_int8_run, _fp8_run, _int4_run):
  *                               a decode call in two halves, the work list built once per step
- *                               and reused by every layer's attention.
+ *                               and reused by every layer's attention;
+ *   pkv_paged_decode_step       store + decode of one step in one call (one launch fewer);
+ *   pkv_paged_attention_decode_noalloc, pkv_paged_attention_decode_status: a decode without a workspace
+ *                               argument; the run status of a workspace.
  *
  * Vocabulary (nano-vllm walkthrough, section 2 context: is_prefill, cu_seqlens_q/k, max_seqlen_q/k,
  * slot_mapping, context_lens, block_tables; "推理运行时", section 分页 KV: logical block j of a
@@ -124,6 +127,24 @@ pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *qu
                                       int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
                                       int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
                                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_decode_step: one decode step of a layer in one call: pkv_kv_cache_store of each sequence's new token
+ * (key, value [num_seqs][num_kv_heads][head_dim]; slot_mapping device int32 [num_seqs], slot < 0 writes
+ * nothing) followed by pkv_paged_attention_decode over the same caches, with the same results (bit-identical
+ * caches and outputs). The store's rows move in the same launch as the decode's work-list plan (the plan reads
+ * only context_lens, the store writes only cache rows), which saves a launch per step. Arguments, layouts,
+ * workspace and errors are those of the two calls; key and value must be 16-byte aligned.
+ * Source: the store-then-attend order of a decode step (nano-vllm walkthrough, section 2 context: slot_mapping
+ * names where each new token's K/V go before attention reads the cache; "LLM Infra 101 v0.2: KV Cache",
+ * section 推理: the new token attends to the cache and itself).
+ */
+pkv_status pkv_paged_decode_step(pkv_dtype dtype, const void *key, const void *value, const int32_t *slot_mapping,
+                                 void *out, const void *query, void *key_cache, void *value_cache,
+                                 const int32_t *block_tables, int32_t block_table_stride, const int32_t *context_lens,
+                                 int32_t num_seqs, int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * paged_attention_prefill (varlen, chunked). Sequence i owns query rows [cu_seqlens_q[i], cu_seqlens_q[i+1])

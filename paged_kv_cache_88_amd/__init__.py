@@ -45,6 +45,8 @@ def load_library(path: str = LIB_PATH):
         "pkv_kv_cache_gather": [ctypes.c_int, P, P, P, P, P, I32, I32, I32, I32, I64, P],
         "pkv_paged_attention_decode": [ctypes.c_int, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32, I64, F, P,
                                        SZ, P],
+        "pkv_paged_decode_step": [ctypes.c_int, P, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32, I64, F,
+                                  P, SZ, P],
         "pkv_paged_attention_decode_noalloc": [ctypes.c_int, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32,
                                                I64, F, P],
         "pkv_paged_attention_prefill": [ctypes.c_int, P, P, P, P, P, I32, P, P, I32, I32, I32, I32, I32, I32, I32,
@@ -223,6 +225,34 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
 
 
 _CACHE_KINDS = {"elements": 0, "int8": 1, "fp8": 2, "int4": 3}
+
+
+def paged_decode_step(key, value, slot_mapping, out, query, key_cache, value_cache, block_tables, context_lens,
+                      max_context_len, scale, workspace=None, stream=None):
+    """One decode step in one call: ``kv_cache_store(key, value, ..., slot_mapping)`` of each sequence's new token
+    ``[B, Hkv, D]``, then ``paged_attention_decode`` (same results; the store shares a launch with the plan)."""
+    lib = load_library()
+    _dev(key, value, slot_mapping, out, query, key_cache, value_cache, block_tables, context_lens, workspace)
+    _i32(slot_mapping, block_tables, context_lens)
+    nb, hkv, bs, d = key_cache.shape
+    b, hq, d2 = query.shape
+    if d2 != d or out.shape != query.shape or value_cache.shape != key_cache.shape:
+        raise ValueError("query/out must be [B, Hq, D] with the caches' D")
+    if key.shape != (b, hkv, d) or value.shape != key.shape or slot_mapping.shape != (b,):
+        raise ValueError("key/value must be [B, Hkv, D] and slot_mapping [B]")
+    if key.dtype != query.dtype or key_cache.dtype != query.dtype:
+        raise ValueError("key, value, caches and query must share one dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or context_lens.shape != (b,):
+        raise ValueError("block_tables must be [B, stride] and context_lens [B]")
+    ws_need = decode_workspace_size(b, hq, hkv, d, bs, max_context_len)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=query.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pkv_paged_decode_step(_dtype_code(query), _ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(out),
+                                     _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+                                     block_tables.shape[1], _ptr(context_lens), b, int(max_context_len), hq, hkv, d, bs,
+                                     nb, float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
 
 
 def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tables, context_lens, max_context_len,

@@ -119,7 +119,7 @@ struct DecodePlan {
     int max_part_tiles;
     int64_t max_items;
     size_t ws_bytes;
-    size_t off_items, off_info, off_m, off_l, off_o;
+    size_t off_items, off_info, off_red, off_m, off_l, off_o;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -134,11 +134,12 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
     p.max_items = 2 * (int64_t)num_seqs +
                   ((int64_t)DECODE_MAX_WORKERS * DECODE_MIN_STRATA + num_kv_heads - 1) / num_kv_heads +
                   ((int64_t)num_seqs * max_tiles_per_seq + p.max_part_tiles - 1) / p.max_part_tiles;
-    // [ctrl: 256 B][work list][per-sequence info][partials m, l, o]
+    // [ctrl: 256 B][work list][per-sequence info][reduce list][partials m, l, o]
     const size_t n = (size_t)p.max_items * num_heads;
     p.off_items = 256;
     p.off_info = p.off_items + align256((size_t)p.max_items * 16);
-    p.off_m = p.off_info + align256((size_t)num_seqs * 16);
+    p.off_red = p.off_info + align256((size_t)num_seqs * 16);
+    p.off_m = p.off_red + align256((size_t)num_seqs * 4);
     p.off_l = p.off_m + align256(n * sizeof(float));
     p.off_o = p.off_l + align256(n * sizeof(float));
     p.ws_bytes = p.off_o + n * head_dim * sizeof(float);
@@ -274,6 +275,7 @@ pkv_status decode_args(pkv::DecodeArgs &a, pkv_dtype dtype, void *out, const voi
     a.ctrl = (int *)workspace;
     a.items = (int4 *)((char *)workspace + plan.off_items);
     a.seq_info = (int4 *)((char *)workspace + plan.off_info);
+    a.red_list = (int *)((char *)workspace + plan.off_red);
     a.ws_m = (float *)((char *)workspace + plan.off_m);
     a.ws_l = (float *)((char *)workspace + plan.off_l);
     a.ws_o = (float *)((char *)workspace + plan.off_o);
@@ -300,6 +302,31 @@ pkv_status pkv_paged_attention_decode(pkv_dtype dtype, void *out, const void *qu
     if (st != PKV_OK || num_seqs == 0) return st;
     return hip_status(pkv::launch_decode(a, dtype == PKV_BF16, head_dim, num_heads / num_kv_heads, stream),
                       "paged_attention_decode launch");
+}
+
+pkv_status pkv_paged_decode_step(pkv_dtype dtype, const void *key, const void *value, const int32_t *slot_mapping,
+                                 void *out, const void *query, void *key_cache, void *value_cache,
+                                 const int32_t *block_tables, int32_t block_table_stride, const int32_t *context_lens,
+                                 int32_t num_seqs, int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    pkv::DecodeArgs a{};
+    pkv_status st = decode_args(a, dtype, out, query, key_cache, value_cache, block_tables, block_table_stride,
+                                context_lens, num_seqs, max_context_len, num_heads, num_kv_heads, head_dim, block_size,
+                                num_blocks, scale, workspace, workspace_bytes);
+    if (st != PKV_OK || num_seqs == 0) return st;
+    REQUIRE(key && value && slot_mapping, PKV_EINVAL, "null pointer argument");
+    REQUIRE(aligned16(key) && aligned16(value), PKV_EINVAL, "key and value pointers must be 16-byte aligned");
+    a.st_key = key;
+    a.st_value = value;
+    a.st_key_cache = key_cache;
+    a.st_value_cache = value_cache;
+    a.st_slots = slot_mapping;
+    a.st_tokens = num_seqs;
+    a.st_chunks = head_dim * elem_bytes(dtype) / 16;
+    a.st_block_size = block_size;
+    return hip_status(pkv::launch_decode(a, dtype == PKV_BF16, head_dim, num_heads / num_kv_heads, stream),
+                      "paged_decode_step launch");
 }
 
 }  // extern "C"

@@ -30,6 +30,7 @@
 // pairs of the row, and p.v on the weights of two rows rounded to a bf16 pair (fp32 FMAs for fp32
 // data). The group sum is a DPP butterfly; softmax runs in log2 units (exp2 with scale*log2(e) folded
 // in), and the accumulator is rescaled only when some running max of the wave grows.
+#include <algorithm>
 #include <climits>
 
 #include "device_common.h"
@@ -136,25 +137,27 @@ __device__ int plan_exclusive_scan(int v, int *s_wave, int *total) {
 // items[k] = {seq, first token, tokens, partial slot (-1 when the sequence is one part)}, longest first
 // (64-bucket counting sort; order inside a bucket is arbitrary and every unit writes its own output, so
 // results do not depend on it). seq_info[i] = {first partial slot, n_i, len_i, L_i}; ctrl[0] = number of
-// parts (sequences with L_i = 0 have no parts; the reduce kernel writes their zero outputs). One workgroup; thread t owns sequences
-// t + k * PLAN_THREADS, and keeps the first PLAN_REG of them in registers (larger batches re-read
-// seq_info).
+// parts (sequences with L_i = 0 have no parts; the reduce kernel writes their zero outputs). red_list gets
+// the sequences the reduce kernel has work for (split into parts, or empty; ctrl[CTRL_RED] of them, in any
+// order). One workgroup of PLAN_THREADS threads; thread t owns sequences t + k * PLAN_THREADS, and keeps the
+// first PLAN_REG of them in registers (larger batches re-read seq_info).
 constexpr int PLAN_REG = 4;
 
-__global__ void __launch_bounds__(PLAN_THREADS)
-decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int max_context_len, int num_kv_heads,
-                   int workers, int min_strata, int max_tiles, int min_tiles,
-                   int4 *__restrict__ items, int4 *__restrict__ seq_info, int *__restrict__ ctrl, PlanKey key) {
+__device__ void plan_body(const int32_t *__restrict__ context_lens, int num_seqs, int max_context_len, int num_kv_heads,
+                          int workers, int min_strata, int max_tiles, int min_tiles, int4 *__restrict__ items,
+                          int4 *__restrict__ seq_info, int *__restrict__ red_list, int *__restrict__ ctrl,
+                          const PlanKey &key) {
     __shared__ int s_wave[PLAN_WAVES];
     __shared__ int hist[PLAN_BUCKETS];
     __shared__ int offs[PLAN_BUCKETS];
-    __shared__ int s_tiles, s_maxlen, s_umin;
+    __shared__ int s_tiles, s_maxlen, s_umin, s_red;
     const int tid = threadIdx.x;
     if (tid < PLAN_BUCKETS) hist[tid] = 0;
     if (tid == 0) {
         s_tiles = 0;
         s_maxlen = 1;
         s_umin = -1;
+        s_red = 0;
     }
     auto clen = [&](int i) { return max(0, min(context_lens[i], max_context_len)); };
     const bool wave_lead = (tid & 63) == 0;
@@ -264,6 +267,7 @@ decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int m
     }
     __syncthreads();
     auto emit = [&](int i, const int4 &si) {      // n - 1 full parts share a bucket: one reservation
+        if (si.y != 1) red_list[atomicAdd(&s_red, 1)] = i;    // split or empty: the reduce kernel's work
         if (si.y <= 0) return;
         const int pfull = si.y > 1 ? atomicAdd(&offs[bucket(si.z)], si.y - 1) : 0;
         for (int p = 0; p + 1 < si.y; ++p) items[pfull + p] = make_int4(i, p * si.z, si.z, si.x + p);
@@ -274,6 +278,36 @@ decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int m
     for (int k = 0; k < PLAN_REG; ++k)
         if (tid + k * PLAN_THREADS < num_seqs) emit(tid + k * PLAN_THREADS, sreg[k]);
     for (int i = tid + PLAN_REG * PLAN_THREADS; i < num_seqs; i += PLAN_THREADS) emit(i, seq_info[i]);
+    __syncthreads();
+    if (tid == 0) ctrl[CTRL_RED] = s_red;
+}
+
+__global__ void __launch_bounds__(PLAN_THREADS)
+decode_plan_kernel(const int32_t *__restrict__ context_lens, int num_seqs, int max_context_len, int num_kv_heads,
+                   int workers, int min_strata, int max_tiles, int min_tiles, int4 *__restrict__ items,
+                   int4 *__restrict__ seq_info, int *__restrict__ red_list, int *__restrict__ ctrl, PlanKey key) {
+    plan_body(context_lens, num_seqs, max_context_len, num_kv_heads, workers, min_strata, max_tiles, min_tiles, items,
+              seq_info, red_list, ctrl, key);
+}
+
+// A decode step's store and plan in one launch: workgroup 0 builds the plan (it reads only context_lens),
+// the others move the new rows into their slots (the store kernel's work, PLAN_THREADS pieces each). The two
+// touch disjoint memory, and the decode kernel that reads both follows in stream order.
+template <int CHUNKS>
+__global__ void __launch_bounds__(PLAN_THREADS)
+store_and_plan_kernel(const u32x4 *__restrict__ key, const u32x4 *__restrict__ value, u32x4 *__restrict__ key_cache,
+                      u32x4 *__restrict__ value_cache, const int32_t *__restrict__ slot_mapping, int64_t num_rows,
+                      int block_size, int num_blocks,
+                      const int32_t *__restrict__ context_lens, int num_seqs, int max_context_len, int num_kv_heads,
+                      int workers, int min_strata, int max_tiles, int min_tiles, int4 *__restrict__ items,
+                      int4 *__restrict__ seq_info, int *__restrict__ red_list, int *__restrict__ ctrl, PlanKey pkey) {
+    if (blockIdx.x == 0) {
+        plan_body(context_lens, num_seqs, max_context_len, num_kv_heads, workers, min_strata, max_tiles, min_tiles,
+                  items, seq_info, red_list, ctrl, pkey);
+        return;
+    }
+    store_piece<CHUNKS>((int64_t)(blockIdx.x - 1) * PLAN_THREADS + threadIdx.x, key, value, key_cache, value_cache,
+                        slot_mapping, num_rows, num_kv_heads, block_size, num_blocks);
 }
 
 template <bool BF16, int D, int G, int NV_, int R_, int NW_>
@@ -1055,90 +1089,112 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
 }
 
 // Merge the parts of each (sequence, head): M = max_p m_p, w_p = 2^(m_p - M),
-// out = sum_p w_p o_p / sum_p w_p l_p. A workgroup serves `hpb` heads of one sequence (hpb in {1, 2, 4, 8},
-// chosen so the grid has a few thousand workgroups: with many sequences most have one part and their
-// workgroups exit after one load). Its threads are hpb heads x PL = 8 / hpb part lanes x D/4 dim groups:
-// a thread merges dims 4 dg .. +4 of the parts p = pl mod PL with 16-byte loads (running max, so each
-// part's m, l, o load in one round trip), and the part lanes are merged through LDS by the same rule.
-// Sequences of one part were written by the decode kernel; empty ones get zeros here.
+// out = sum_p w_p o_p / sum_p w_p l_p. The plan lists the sequences with work here (split into parts, or
+// empty: those get zeros); workgroup (x, y) serves heads x * hpb .. + hpb of list entries y, y + Y, ...
+// (hpb in {1, 2, 4, 8}). Its threads are hpb heads x PL = 8 / hpb part lanes x D/4 dim groups: a thread merges
+// dims 4 dg .. +4 of the parts p = pl mod PL with 16-byte loads (running max, so each part's m, l, o load in
+// one round trip), and the part lanes are merged through LDS by the same rule. Sequences of one part were
+// written by the decode kernel; when none is split or empty the list is empty and every workgroup exits
+// after one load.
 constexpr int REDUCE_THREADS = 256;
+constexpr int REDUCE_WGS = 1024;             // workgroups the reduce grid aims at
 
 template <bool BF16, int D>
 __global__ void __launch_bounds__(REDUCE_THREADS)
-decode_reduce_kernel(void *__restrict__ out, const int4 *__restrict__ seq_info, int num_heads, int hpb,
-                     const float *__restrict__ ws_m, const float *__restrict__ ws_l, const float *__restrict__ ws_o,
-                     int *__restrict__ ctrl, PlanKey key) {
+decode_reduce_kernel(void *__restrict__ out, const int4 *__restrict__ seq_info, const int *__restrict__ red_list,
+                     int num_heads, int hpb, const float *__restrict__ ws_m, const float *__restrict__ ws_l,
+                     const float *__restrict__ ws_o, int *__restrict__ ctrl, PlanKey key) {
     constexpr int DG = D / 4, SLOTS = REDUCE_THREADS / DG;          // SLOTS = head slots x part lanes
     __shared__ f32x4 s_o[SLOTS][DG];
     __shared__ float s_l[SLOTS], s_m[SLOTS];
     if (!plan_key_ok(ctrl, key)) return;
-    const int seq = blockIdx.y;
-    const int4 si = seq_info[seq];
-    const int nparts = si.y;
-    if (nparts == 0) {                           // empty context: zero outputs for this workgroup's heads
-        const int h0 = blockIdx.x * hpb, nh = min(hpb, num_heads - h0);
-        const int64_t base = ((int64_t)seq * num_heads + h0) * D;
-        for (int e = threadIdx.x; e < nh * D; e += REDUCE_THREADS) {
-            if constexpr (BF16) ((uint16_t *)out)[base + e] = 0;
-            else ((float *)out)[base + e] = 0.f;
-        }
-        return;
-    }
-    if (nparts == 1) return;
+    const int count = ctrl[CTRL_RED];
     const int PL = SLOTS / hpb;
     const int t = threadIdx.x, slot = t / DG, dg = t % DG;
     const int hs = slot / PL, pl = slot % PL;
     const int head = blockIdx.x * hpb + hs;
     const bool active = head < num_heads;
-    float ll = 0.f;
-    f32x4 oo = {0.f, 0.f, 0.f, 0.f};
-    // one pass per part lane with a running max (each part's m, l and o load together), then the part
-    // lanes are merged with the same rule through LDS
-    float mm = M_INIT;
-    if (active) {
-        const int64_t p0 = (int64_t)si.x * num_heads + head;     // part p sits at p0 + p * num_heads
-#pragma unroll 2
-        for (int p = pl; p < nparts; p += PL) {
-            const int64_t pi = p0 + (int64_t)p * num_heads;
-            const float mp = ws_m[pi], lp = ws_l[pi];
-            const f32x4 op = *(const f32x4 *)(ws_o + pi * D + 4 * dg);
-            const float mn = fmaxf(mm, mp);
-            const float a = fast_exp2(mm - mn), w = fast_exp2(mp - mn);
-            ll = ll * a + lp * w;
-            oo = oo * a + op * w;
-            mm = mn;
+    for (int e = blockIdx.y; e < count; e += gridDim.y) {           // uniform over the workgroup
+        const int seq = red_list[e];
+        const int4 si = seq_info[seq];
+        const int nparts = si.y;
+        if (nparts == 0) {                       // empty context: zero outputs for this workgroup's heads
+            const int h0 = blockIdx.x * hpb, nh = min(hpb, num_heads - h0);
+            const int64_t base = ((int64_t)seq * num_heads + h0) * D;
+            for (int x = t; x < nh * D; x += REDUCE_THREADS) {
+                if constexpr (BF16) ((uint16_t *)out)[base + x] = 0;
+                else ((float *)out)[base + x] = 0.f;
+            }
+            continue;
         }
-    }
-    s_o[slot][dg] = oo;
-    if (dg == 0) {
-        s_l[slot] = ll;
-        s_m[slot] = mm;
-    }
-    __syncthreads();
-    if (pl != 0 || !active) return;
-    for (int q = 1; q < PL; ++q) {
-        const float mq = s_m[slot + q], mn = fmaxf(mm, mq);
-        const float a = fast_exp2(mm - mn), w = fast_exp2(mq - mn);
-        oo = oo * a + s_o[slot + q][dg] * w;
-        ll = ll * a + s_l[slot + q] * w;
-        mm = mn;
-    }
-    const float inv = 1.0f / ll;
-    const int64_t o = ((int64_t)seq * num_heads + head) * D + 4 * dg;
-    if constexpr (BF16) {
-        *(uint2 *)((uint16_t *)out + o) = make_uint2(pack_bf16x2(oo[0] * inv, oo[1] * inv), pack_bf16x2(oo[2] * inv, oo[3] * inv));
-    } else {
-        *(f32x4 *)((float *)out + o) = oo * inv;
+        float ll = 0.f;
+        f32x4 oo = {0.f, 0.f, 0.f, 0.f};
+        // one pass per part lane with a running max (each part's m, l and o load together), then the part
+        // lanes are merged with the same rule through LDS
+        float mm = M_INIT;
+        if (active) {
+            const int64_t p0 = (int64_t)si.x * num_heads + head;     // part p sits at p0 + p * num_heads
+#pragma unroll 2
+            for (int p = pl; p < nparts; p += PL) {
+                const int64_t pi = p0 + (int64_t)p * num_heads;
+                const float mp = ws_m[pi], lp = ws_l[pi];
+                const f32x4 op = *(const f32x4 *)(ws_o + pi * D + 4 * dg);
+                const float mn = fmaxf(mm, mp);
+                const float a = fast_exp2(mm - mn), w = fast_exp2(mp - mn);
+                ll = ll * a + lp * w;
+                oo = oo * a + op * w;
+                mm = mn;
+            }
+        }
+        s_o[slot][dg] = oo;
+        if (dg == 0) {
+            s_l[slot] = ll;
+            s_m[slot] = mm;
+        }
+        __syncthreads();
+        if (pl == 0 && active) {
+            for (int q = 1; q < PL; ++q) {
+                const float mq = s_m[slot + q], mn = fmaxf(mm, mq);
+                const float a = fast_exp2(mm - mn), w = fast_exp2(mq - mn);
+                oo = oo * a + s_o[slot + q][dg] * w;
+                ll = ll * a + s_l[slot + q] * w;
+                mm = mn;
+            }
+            const float inv = 1.0f / ll;
+            const int64_t o = ((int64_t)seq * num_heads + head) * D + 4 * dg;
+            if constexpr (BF16) {
+                *(uint2 *)((uint16_t *)out + o) = make_uint2(pack_bf16x2(oo[0] * inv, oo[1] * inv),
+                                                             pack_bf16x2(oo[2] * inv, oo[3] * inv));
+            } else {
+                *(f32x4 *)((float *)out + o) = oo * inv;
+            }
+        }
+        __syncthreads();                        // s_o, s_l, s_m are rewritten by the next entry
     }
 }
 
 // The plan kernel, sizing parts for the resident waves of the decode kernel that will run: the matrix-core
 // kernel runs one workgroup of DECODE_CU_WAVES_BF16 / _Q8 waves per compute unit, the other a.workers.
+// With a decode step's store (a.st_chunks > 0) the plan shares its launch with the store's pieces.
 static hipError_t launch_plan(const DecodeArgs &a, bool mfma, bool q8, hipStream_t stream) {
     const int workers = mfma ? a.compute_units * (q8 ? DECODE_CU_WAVES_Q8 : DECODE_CU_WAVES_BF16) : a.workers;
+    if (a.st_chunks > 0) {
+        const int64_t rows = a.st_tokens * a.num_kv_heads, pieces = rows * a.st_chunks;
+        const dim3 grid((unsigned)(1 + (pieces + PLAN_THREADS - 1) / PLAN_THREADS));
+        auto k = (const u32x4 *)a.st_key, v = (const u32x4 *)a.st_value;
+        auto kc = (u32x4 *)a.st_key_cache, vc = (u32x4 *)a.st_value_cache;
+        auto kern = a.st_chunks == 8 ? store_and_plan_kernel<8> : a.st_chunks == 16 ? store_and_plan_kernel<16>
+                                                                                   : store_and_plan_kernel<32>;
+        if (a.st_chunks != 8 && a.st_chunks != 16 && a.st_chunks != 32) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(kern, grid, dim3(PLAN_THREADS), 0, stream, k, v, kc, vc, a.st_slots, rows,
+                           a.st_block_size, (int)a.num_blocks, a.context_lens, a.num_seqs, a.max_context_len,
+                           a.num_kv_heads, workers, a.min_strata, a.max_part_tiles, a.min_part_tiles, a.items,
+                           a.seq_info, a.red_list, a.ctrl, a.key);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, a.context_lens, a.num_seqs,
                        a.max_context_len, a.num_kv_heads, workers, a.min_strata, a.max_part_tiles, a.min_part_tiles,
-                       a.items, a.seq_info, a.ctrl, a.key);
+                       a.items, a.seq_info, a.red_list, a.ctrl, a.key);
     return hipGetLastError();
 }
 
@@ -1173,13 +1229,15 @@ static hipError_t launch_decode_cfg(const DecodeArgs &a, hipStream_t stream) {
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // heads per reduce workgroup: the fewest (1..8) that keep the grid at ~2048 workgroups or more
+    // heads per reduce workgroup: the fewest (1..8) that keep (head groups) x (sequences) at REDUCE_WGS or
+    // more; list entries per column: enough columns that the grid holds about REDUCE_WGS workgroups
     const int num_heads = a.num_kv_heads * G;
     int hpb = 8;
-    while (hpb > 1 && (int64_t)((num_heads + hpb - 1) / hpb) * a.num_seqs < 2048) hpb >>= 1;
-    hipLaunchKernelGGL((decode_reduce_kernel<BF16, D>), dim3((num_heads + hpb - 1) / hpb, a.num_seqs),
-                       dim3(REDUCE_THREADS), 0, stream, a.out, a.seq_info, num_heads, hpb, a.ws_m, a.ws_l, a.ws_o,
-                       a.ctrl, a.key);
+    while (hpb > 1 && (int64_t)((num_heads + hpb - 1) / hpb) * a.num_seqs < REDUCE_WGS) hpb >>= 1;
+    const int hgroups = (num_heads + hpb - 1) / hpb;
+    const int cols = (int)std::min<int64_t>(a.num_seqs, std::max(1, REDUCE_WGS / hgroups));
+    hipLaunchKernelGGL((decode_reduce_kernel<BF16, D>), dim3(hgroups, cols), dim3(REDUCE_THREADS), 0, stream, a.out,
+                       a.seq_info, a.red_list, num_heads, hpb, a.ws_m, a.ws_l, a.ws_o, a.ctrl, a.key);
     return hipGetLastError();
 }
 

@@ -116,4 +116,30 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                    c, 0, 0, 0);
 }
 
+// One 16-byte piece of the store: thread gid moves piece gid % CHUNKS of row gid / CHUNKS (row = token *
+// num_kv_heads + kv head) from the new rows to the slot's row of the cache; slots < 0 and slots outside the
+// pool move nothing. Consecutive threads take consecutive pieces of a row.
+template <int CHUNKS>
+__device__ __forceinline__ void store_piece(int64_t gid, const u32x4 *__restrict__ key, const u32x4 *__restrict__ value,
+                                            u32x4 *__restrict__ key_cache, u32x4 *__restrict__ value_cache,
+                                            const int32_t *__restrict__ slot_mapping, int64_t num_rows,
+                                            int num_kv_heads, int block_size, int num_blocks) {
+    const int64_t row = gid / CHUNKS;
+    if (row >= num_rows) return;
+    const int chunk = (int)(gid % CHUNKS);
+    const int64_t token = row / num_kv_heads;
+    const int kvh = (int)(row % num_kv_heads);
+    const int32_t slot = slot_mapping[token];
+    if (slot < 0) return;                          // padding token: nothing to write
+    if (slot / block_size >= num_blocks) return;   // outside the pool: precondition broken, skip
+    const int64_t block = slot / block_size;
+    const int off = slot % block_size;
+    const int64_t dst = cache_row(block, kvh, off, num_kv_heads, block_size) * CHUNKS + chunk;
+    const int64_t src = row * CHUNKS + chunk;
+    const u32x4 k = __builtin_nontemporal_load(key + src);
+    const u32x4 v = __builtin_nontemporal_load(value + src);
+    key_cache[dst] = k;
+    value_cache[dst] = v;
+}
+
 }  // namespace pkv

@@ -35,6 +35,7 @@ struct PlanKey {
 };
 constexpr int PLAN_KEY_MAGIC = 0x504b5650;
 constexpr int CTRL_PARTS = 0;          // int32 words of the 256-byte control block
+constexpr int CTRL_RED = 1;            // entries of the reduce list
 constexpr int CTRL_KEY = 8;            // [8, 16): the plan's key
 constexpr int CTRL_ERR = 16;           // 0 after a plan; 1 once a run found a key other than its own
 
@@ -61,6 +62,7 @@ struct DecodeArgs {
     float scale_log2e;
     int4 *items;           // work list, [max_items]
     int4 *seq_info;        // [num_seqs]: first partial slot, parts, part length, length
+    int *red_list;         // [num_seqs]: sequences the reduce kernel serves (split, or empty), ctrl[CTRL_RED] of them
     int *ctrl;             // ctrl[0] = number of parts
     float *ws_m;           // [max_items][num_heads]
     float *ws_l;           // [max_items][num_heads]
@@ -71,6 +73,15 @@ struct DecodeArgs {
     bool int4_codes = false;              // quantized caches: 4-bit codes (two per byte) instead of int8
     bool run_only = false;                // decode and reduce from a work list already in the workspace
     PlanKey key{};                        // written by the plan, checked by the run
+    // A decode step with its store (pkv_paged_decode_step): the store's rows move in the plan's launch.
+    const void *st_key = nullptr;         // new rows [st_tokens][num_kv_heads][row bytes]
+    const void *st_value = nullptr;
+    void *st_key_cache = nullptr;
+    void *st_value_cache = nullptr;
+    const int32_t *st_slots = nullptr;    // [st_tokens]
+    int64_t st_tokens = 0;
+    int st_chunks = 0;                    // 16-byte pieces per row (8, 16 or 32); 0: no store in this call
+    int st_block_size = 0;
 };
 
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, int head_dim, int group, hipStream_t stream);

@@ -20,23 +20,8 @@ __global__ void __launch_bounds__(256) store_kernel(const u32x4 *__restrict__ ke
                                                     u32x4 *__restrict__ key_cache, u32x4 *__restrict__ value_cache,
                                                     const int32_t *__restrict__ slot_mapping, int64_t num_rows,
                                                     int num_kv_heads, int block_size, int num_blocks) {
-    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    int64_t row = gid / CHUNKS;            // row = token * num_kv_heads + kv head
-    if (row >= num_rows) return;
-    int chunk = (int)(gid % CHUNKS);
-    int64_t token = row / num_kv_heads;
-    int kvh = (int)(row % num_kv_heads);
-    int32_t slot = slot_mapping[token];
-    if (slot < 0) return;                  // padding token: nothing to write
-    if (slot / block_size >= num_blocks) return;   // outside the pool: precondition broken, skip
-    int64_t block = slot / block_size;
-    int off = slot % block_size;
-    int64_t dst = cache_row(block, kvh, off, num_kv_heads, block_size) * CHUNKS + chunk;
-    int64_t src = row * CHUNKS + chunk;
-    u32x4 k = __builtin_nontemporal_load(key + src);
-    u32x4 v = __builtin_nontemporal_load(value + src);
-    key_cache[dst] = k;
-    value_cache[dst] = v;
+    store_piece<CHUNKS>((int64_t)blockIdx.x * blockDim.x + threadIdx.x, key, value, key_cache, value_cache,
+                        slot_mapping, num_rows, num_kv_heads, block_size, num_blocks);
 }
 
 template <int CHUNKS>

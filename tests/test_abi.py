@@ -208,6 +208,23 @@ def test_decode_noalloc_validation(lib):
     assert f(1, None, None, None, None, None, 4, None, 0, 64, 8, 2, 128, 16, 64, 0.1, None) == 0     # no-op
 
 
+def test_decode_step_validation(lib):
+    """The one-call decode step refuses what the store and the decode refuse, before any launch."""
+    f = lib.pkv_paged_decode_step
+    need = lib.pkv_paged_attention_decode_workspace_size(2, 8, 2, 128, 16, 64)
+    ws = ctypes.c_void_p(1 << 24)
+    # (dtype, key, value, slots, out, q, kc, vc, bt, stride, context_lens, B, max_len, Hq, Hkv, D, bs, NB, scale,
+    #  workspace, bytes, stream)
+    assert f(1, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 8, 2, 128, 16, 64, 0.1, ws, need,
+             None) == 1                                                                          # null key
+    assert f(1, ctypes.c_void_p((1 << 20) + 8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 8, 2, 128,
+             16, 64, 0.1, ws, need, None) == 1                                                  # misaligned key
+    assert f(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 8, 2, 96, 16, 64, 0.1, ws, need,
+             None) == 2                                                                          # head_dim
+    assert f(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 8, 2, 128, 16, 64, 0.1, ws, need - 1,
+             None) == 3                                                                          # workspace
+
+
 def test_binding_fails_loudly_without_library(pkv, tmp_path):
     saved = pkv._lib
     try:
