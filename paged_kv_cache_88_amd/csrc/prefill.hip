@@ -50,6 +50,9 @@ constexpr float PF_RESCALE_SLACK = 8.0f;  // weights stay <= 256 between rescale
 constexpr int PF_RANK_MAX = 64;           // batches ranked by length for the dispatch order
 constexpr int PF_XCDS = 8;                // MI355X: 8 XCDs, each with its own L2
 constexpr int PF_BUF_W3 = 0x00020000;     // buffer descriptor word 3: raw, untyped buffer (gfx9 family)
+constexpr int PF_KAHEAD = 4;              // K operand reads in flight ahead of the S^T MFMAs
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int SGB_MFMA = 0x008, SGB_DS_READ = 0x100;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -283,18 +286,35 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
         const int key0 = kt * PF_BN, cur = kt & 1;
         if (kt + 1 < ntiles) load_tile(key0 + PF_BN);      // in flight during this tile's math
 
-        // S^T = K Q^T: s[kb][qb] holds keys 16*kb + 4*lb + i of row 16*qb + lr
+        // S^T = K Q^T: s[kb][qb] holds keys 16*kb + 4*lb + i of row 16*qb + lr. The 16 K operands (step
+        // t = 4 kb + ks) are read PF_KAHEAD steps ahead of the MFMAs that take them; the scheduling groups
+        // below keep that order (left alone, the compiler waits on every second read).
         f32x4 s[4][QB];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+            u32x4 ka[PF_KAHEAD];
+            auto kread = [&](int t) {
+                return *(const u32x4 *)&sK[cur][((t >> 2) * 16 + lr) * PF_KPAD + lb * 8 + (t & 3) * 32];
+            };
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const u32x4 ka = *(const u32x4 *)&sK[cur][(kb * 16 + lr) * PF_KPAD + lb * 8 + ks * 32];
+            for (int t = 0; t < PF_KAHEAD; ++t) ka[t] = kread(t);
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma16x16x32(ka, qb_reg[qb][ks], s[kb][qb]);
+            for (int t = 0; t < 16; ++t) {
+                const u32x4 a = ka[t % PF_KAHEAD];
+                if (t + PF_KAHEAD < 16) ka[t % PF_KAHEAD] = kread(t + PF_KAHEAD);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) s[t >> 2][qb] = mfma16x16x32(a, qb_reg[qb][t & 3], s[t >> 2][qb]);
             }
+            __builtin_amdgcn_sched_group_barrier(SGB_DS_READ, PF_KAHEAD, 0);
+#pragma unroll
+            for (int t = 0; t < 16 - PF_KAHEAD; ++t) {
+                __builtin_amdgcn_sched_group_barrier(SGB_MFMA, QB, 0);
+                __builtin_amdgcn_sched_group_barrier(SGB_DS_READ, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(SGB_MFMA, QB * PF_KAHEAD, 0);
         }
 
         // 8-bit caches: each score times its key's scale (keys 16 kb + 4 lb + i), before the mask
