@@ -12,8 +12,8 @@ R * step bytes >> the last-level cache), so K/V come from HBM, not from cache.
 
 Prints one JSON line (rank 0): value = algorithmic bytes of the step / step time (GB/s, wall clock
 over the timed steps), plus the roofline of the decode call measured with HIP events on the launch
-stream (recorded around every fourth decode call of the timed steps: each event costs the stream
-about 5 us, so recording them around every call would slow the steps it measures), and the CPU oracle's rate
+stream (recorded around runs of ten back-to-back calls: each event costs the stream a few microseconds, so
+recording them around every call would slow the calls it measures), and the CPU oracle's rate
 on a bounded sample of the same workload. Secondary legs (not part of `value`): the same decode over
 int8, fp8 (E4M3) and int4 caches; the decode call on the other two decode workloads (batch 64 at block 256,
 batch 16 at 16k-32k tokens); the chunked-prefill workload on MFMA (bf16, int8 and fp8 caches); and the
@@ -78,7 +78,8 @@ Q8_LEGS = {
 
 def bench_q8(kind, pkv, torch, W, c, dev, copies, steps, warmup):
     """The same decode workload over a quantized cache (rows quantized by the library's store from the bf16
-    values; pool copies rotated as in the main leg): average decode-call time from HIP events."""
+    values; pool copies rotated as in the main leg): average decode-call time from HIP events around runs of
+    back-to-back calls."""
     what, store_name, decode_name = Q8_LEGS[kind]
     store, decode = getattr(pkv, store_name), getattr(pkv, decode_name)
     kr, vr, slots = W.cached_rows(c.pool)
@@ -104,16 +105,21 @@ def bench_q8(kind, pkv, torch, W, c, dev, copies, steps, warmup):
     ws = torch.empty(pkv.decode_workspace_size(c.num_seqs, c.num_heads, c.num_kv_heads, c.head_dim, c.block_size,
                                                c.max_context_len), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for k in range(warmup + steps):
+    batch = 10                                # back-to-back calls between an event pair
+    for k in range(warmup):
         kc, vc, ks, vs = pools[k % copies]
-        if k >= warmup:
-            ev[k - warmup][0].record(stream)
         decode(out, q, kc, vc, ks, vs, bt, cl, c.max_context_len, c.scale, workspace=ws, stream=stream)
-        if k >= warmup:
-            ev[k - warmup][1].record(stream)
+    runs = []
+    for b in range(0, steps, batch):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(b, min(steps, b + batch)):
+            kc, vc, ks, vs = pools[k % copies]
+            decode(out, q, kc, vc, ks, vs, bt, cl, c.max_context_len, c.scale, workspace=ws, stream=stream)
+        e1.record(stream)
+        runs.append((e0, e1, min(steps, b + batch) - b))
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms = float(np.mean([a.elapsed_time(z) / n for a, z, n in runs]))
     nbytes = decode_bytes_q4(c) if kind == "int4" else decode_bytes_q8(c)
     return {"workload": c.name, "cache": what,
             "decode_ms": round(ms, 5), "algorithmic_bytes": nbytes,
@@ -263,7 +269,7 @@ def bench_ceilings(pkv, torch, dev, reps=10):
 
 def bench_decode_workload(pkv, torch, W, cfg, dev, steps, warmup):
     """The decode call alone on another decode workload (pool copies rotated so K/V come from HBM): HIP
-    events around every call."""
+    events around runs of back-to-back calls."""
     c = W.make_config(cfg)
 
     def tt(a):
@@ -291,16 +297,22 @@ def bench_decode_workload(pkv, torch, W, cfg, dev, steps, warmup):
     ws = torch.empty(pkv.decode_workspace_size(c.num_seqs, c.num_heads, c.num_kv_heads, c.head_dim, c.block_size,
                                                c.max_context_len), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for k in range(warmup + steps):
+    batch = 10                                # back-to-back calls between an event pair
+    for k in range(warmup):
         kc, vc = pools[k % copies]
-        if k >= warmup:
-            ev[k - warmup][0].record(stream)
         pkv.paged_attention_decode(out, q, kc, vc, bt, cl, c.max_context_len, c.scale, workspace=ws, stream=stream)
-        if k >= warmup:
-            ev[k - warmup][1].record(stream)
+    runs = []
+    for b in range(0, steps, batch):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(b, min(steps, b + batch)):
+            kc, vc = pools[k % copies]
+            pkv.paged_attention_decode(out, q, kc, vc, bt, cl, c.max_context_len, c.scale, workspace=ws,
+                                       stream=stream)
+        e1.record(stream)
+        runs.append((e0, e1, min(steps, b + batch) - b))
     torch.cuda.synchronize()
-    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms = np.array([a.elapsed_time(z) / n for a, z, n in runs])
     gbs = nbytes / (ms.mean() * 1e-3) / 1e9
     res = {"workload": c.name, "num_seqs": c.num_seqs, "sum_context_tokens": int(c.context_lens.sum()),
            "block_size": c.block_size, "num_heads": c.num_heads, "num_kv_heads": c.num_kv_heads,
@@ -477,22 +489,28 @@ def main():
                                      c.max_context_len)
     ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    # A recorded event costs the stream about 5 us, so the timed steps bracket only every EVERY-th decode
-    # call with events (the call's duration for the roofline, from the timed region itself); the store's
-    # duration comes from an untimed pass after it.
-    EVERY = 4
-    sampled = list(range(0, args.steps, EVERY))
-    ev0 = {k: torch.cuda.Event(enable_timing=True) for k in sampled}       # decode start
-    ev1 = {k: torch.cuda.Event(enable_timing=True) for k in sampled}       # decode end
+    # A recorded event costs the stream a few microseconds, so durations come from event pairs around runs of
+    # back-to-back calls (BATCH calls per pair), never around single calls.
+    BATCH = 10
 
-    def step(k, timed=False):
+    def step(k):
         kc, vc = pools[k % copies]
         pkv.kv_cache_store(kn, vn, kc, vc, sm, stream=stream)
-        if timed and k in ev0:
-            ev0[k].record(stream)
         pkv.paged_attention_decode(out, q, kc, vc, bt, cl, c.max_context_len, c.scale, workspace=ws, stream=stream)
-        if timed and k in ev1:
-            ev1[k].record(stream)
+
+    def batched_ms(call, calls):
+        """Average duration of call(k) over `calls` back-to-back calls: event pairs around runs of BATCH."""
+        runs = []
+        for b in range(0, calls, BATCH):
+            n = min(BATCH, calls - b)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for k in range(b, b + n):
+                call(k)
+            e1.record(stream)
+            runs.append((e0, e1, n))
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(z) / n for a, z, n in runs])
 
     def one_call_step(k):
         kc, vc = pools[k % copies]
@@ -511,58 +529,53 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # the same step as two calls (kv_cache_store, then paged_attention_decode): wall clock, and the decode
-    # call's duration for the roofline from events around every EVERY-th call
+    # the same step as two calls (kv_cache_store, then paged_attention_decode): wall clock
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(k, timed=True)
+        step(k)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_two_calls = (t1 - t0) * 1e3 / args.steps
-    dec_ms = np.array([ev0[k].elapsed_time(ev1[k]) for k in sampled])
+
+    # the decode call alone, back to back (pool copies rotated), for the roofline: events around runs of
+    # BATCH calls; the call is plan + decode + reduce kernels
+    def decode_call(k):
+        kc, vc = pools[k % copies]
+        pkv.paged_attention_decode(out, q, kc, vc, bt, cl, c.max_context_len, c.scale, workspace=ws, stream=stream)
+
+    for k in range(args.warmup):
+        decode_call(k)
+    dec_ms = batched_ms(decode_call, args.steps)
     dec_avg_ms = float(dec_ms.mean())
     def dist(x):
         return {"mean": round(float(x.mean()), 5), "median": round(float(np.median(x)), 5),
                 "p10": round(float(np.percentile(x, 10)), 5), "p90": round(float(np.percentile(x, 90)), 5)}
     achieved = decode_bytes(c) / (dec_avg_ms * 1e-3) / 1e9
     finite = bool(torch.isfinite(out.float()).all().item())
-    # store alone (untimed pass): events around each store
-    st0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    st1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for k in range(args.steps):
+    # store alone, back to back
+    def store_call(k):
         kc, vc = pools[k % copies]
-        st0[k].record(stream)
         pkv.kv_cache_store(kn, vn, kc, vc, sm, stream=stream)
-        st1[k].record(stream)
-    torch.cuda.synchronize()
-    store_ms = np.array([a.elapsed_time(b) for a, b in zip(st0, st1)])
-    # the same decode in two halves (untimed pass): one plan, then runs from it, as a model's layers would
-    # (a second, identical plan halfway is timed: queued behind a run, its events measure the GPU alone)
-    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    r0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    r1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
-    def plan():
+    store_ms = batched_ms(store_call, args.steps)
+    # the same decode in two halves: one plan, then runs from it, as a model's layers would; plans back to
+    # back are timed the same way
+    def plan(k=0):
         pkv.paged_attention_decode_plan(cl, c.max_context_len, c.num_heads, c.num_kv_heads, c.head_dim,
                                         c.block_size, ws, dtype=td, stream=stream)
 
-    plan()
-    for k in range(args.steps):
+    def run_call(k):
         kc, vc = pools[k % copies]
-        r0[k].record(stream)
         pkv.paged_attention_decode_run(out, q, kc, vc, bt, c.max_context_len, c.scale, ws, stream=stream)
-        r1[k].record(stream)
-        if k == args.steps // 2:
-            p0.record(stream)
-            plan()
-            p1.record(stream)
-    torch.cuda.synchronize()
-    plan_run = {"plan_ms": round(p0.elapsed_time(p1), 5),
-                "run_ms": dist(np.array([a.elapsed_time(b) for a, b in zip(r0, r1)])),
-                "what": "paged_attention_decode_plan once, then paged_attention_decode_run per call (untimed pass)"}
+
+    plan_ms = batched_ms(plan, 2 * BATCH)
+    run_ms = batched_ms(run_call, args.steps)
+    plan_run = {"plan_ms": round(float(plan_ms.mean()), 5), "run_ms": dist(run_ms),
+                "what": "paged_attention_decode_plan, then paged_attention_decode_run per call from it "
+                        f"(runs of {BATCH} back-to-back calls between event pairs)"}
 
 
     result = {
@@ -590,12 +603,11 @@ def main():
                 "call (the store shares a launch with the decode's plan)",
         "two_calls": {"ms_per_step": round(ms_two_calls, 5),
                       "value": round(step_bytes / (ms_two_calls * 1e-3) / 1e9, 2),
-                      "what": "the same step as kv_cache_store then paged_attention_decode (events around every "
-                              f"{EVERY}th decode call)"},
+                      "what": "the same step as kv_cache_store then paged_attention_decode (wall clock)"},
         "plan_and_runs": plan_run,
         "timing_ms": {"decode_call": dist(dec_ms), "store": dist(store_ms),
-                      "events": f"HIP events on the launch stream: decode call on every {EVERY}th timed step "
-                                f"({len(sampled)} calls), store in an untimed pass after the timed steps"},
+                      "events": f"HIP events on the launch stream around runs of {BATCH} back-to-back calls "
+                                f"({args.steps} calls, pool copies rotated); the distribution is over runs"},
         "roofline": {"bound": "hbm",
                      "kernel": "paged_attention_decode call (decode_plan_kernel + decode_mfma_kernel + decode_reduce_kernel)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

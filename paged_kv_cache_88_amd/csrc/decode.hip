@@ -79,7 +79,10 @@ __device__ __forceinline__ bool plan_key_ok(int *ctrl, const PlanKey &key) {
     return ok;
 }
 
-constexpr int PLAN_THREADS = 1024;
+#ifndef PKV_PLAN_THREADS
+#define PKV_PLAN_THREADS 256      // four waves: fewer waves meet at each of the plan's barriers
+#endif
+constexpr int PLAN_THREADS = PKV_PLAN_THREADS;
 constexpr int PLAN_WAVES = PLAN_THREADS / 64;
 constexpr int PLAN_BUCKETS = 64;
 constexpr int DECODE_TILE = 32;               // part lengths are multiples of this many tokens
