@@ -627,9 +627,21 @@ __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, int b
 // so pair k = ((w >> 4 k) & 0x000f000f) | 0x43004300 holds elements k and k + 4 as 128 + u. With u = q + 8
 // the values are 136 + q; the decode subtracts 136 times the matching sums (I4_BIAS).
 constexpr float I4_BIAS = 136.0f;
+// The mask (in a scalar register) and the exponent bits (in a vector register) are held in registers the
+// compiler cannot see through, so each pair is one v_and_or_b32 (after a shift for K > 0): these encodings
+// take neither a literal nor two scalar operands.
+struct NibbleConsts {
+    uint32_t mask, bits;
+};
+__device__ __forceinline__ NibbleConsts nibble_consts() {
+    NibbleConsts c;
+    asm("s_mov_b32 %0, 0x000f000f" : "=s"(c.mask));
+    asm("v_mov_b32 %0, 0x43004300" : "=v"(c.bits));
+    return c;
+}
 template <int K>
-__device__ __forceinline__ uint32_t nibble_pair_to_bf16x2(uint32_t w) {
-    return ((w >> (4 * K)) & 0x000f000fu) | 0x43004300u;
+__device__ __forceinline__ uint32_t nibble_pair_to_bf16x2(uint32_t w, const NibbleConsts &c) {
+    return ((w >> (4 * K)) & c.mask) | c.bits;
 }
 
 // Registers of one 32-token tile of the matrix-core decode: bf16 rows, or 8-bit codes plus per-row scales,
@@ -831,6 +843,7 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
         }
     };
 
+    const NibbleConsts nc = I4 ? nibble_consts() : NibbleConsts{0u, 0u};
     float m = M_INIT, l = 0.f;
     f32x4 acc[8];
 #pragma unroll
@@ -849,9 +862,7 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
             for (int e = 0; e < 4; ++e) qs = dot2_bf16(w[e], ONES, qs);
             qt[c] = u32x4{pair_lo(w[0], w[2]), pair_hi(w[0], w[2]), pair_lo(w[1], w[3]), pair_hi(w[1], w[3])};
         }
-        qs += __shfl_xor(qs, 16);
-        qs += __shfl_xor(qs, 32);
-        kcorr = I4_BIAS * qs;
+        kcorr = I4_BIAS * lane_blocks_sum(qs);
     };
 
     auto compute = [&](const Unit &x, int tile, Tile &t) {
@@ -859,8 +870,12 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
             if (tile == 0) prep_q();                // the unit's queries arrived with (or before) its first tile
         }
         // masked tokens: past the unit's end (only in its last tile), or in a block outside the pool,
-        // whose rows (block 0) may hold anything: those get V zeroed as well
-        const bool partial = (tile + 1) * TILE > x.ntok || !t.live[0] || !t.live[1];   // wave-uniform
+        // whose rows (block 0) may hold anything: those get V zeroed as well. Group g holds tile tokens
+        // 16 g .. 16 g + 15, of which the first lim[g] (wave-uniform) are real; a lane's token 4 b + i of the
+        // group is kept iff 4 b + i < lim[g] (one compare, no branch).
+        int lim[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) lim[g] = t.live[g] ? x.ntok - (tile * TILE + 16 * g) : 0;
         // bf16 operands of the tile (int8 codes are converted exactly)
         u32x4 tk[2][4], tv[2][4];
 #pragma unroll
@@ -869,14 +884,14 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const uint32_t w = t.k[g][c];
-                    tk[g][c] = u32x4{nibble_pair_to_bf16x2<0>(w), nibble_pair_to_bf16x2<1>(w),
-                                     nibble_pair_to_bf16x2<2>(w), nibble_pair_to_bf16x2<3>(w)};
+                    tk[g][c] = u32x4{nibble_pair_to_bf16x2<0>(w, nc), nibble_pair_to_bf16x2<1>(w, nc),
+                                     nibble_pair_to_bf16x2<2>(w, nc), nibble_pair_to_bf16x2<3>(w, nc)};
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t w = t.v[g][i];
-                    tv[g][i] = u32x4{nibble_pair_to_bf16x2<0>(w), nibble_pair_to_bf16x2<1>(w),
-                                     nibble_pair_to_bf16x2<2>(w), nibble_pair_to_bf16x2<3>(w)};
+                    tv[g][i] = u32x4{nibble_pair_to_bf16x2<0>(w, nc), nibble_pair_to_bf16x2<1>(w, nc),
+                                     nibble_pair_to_bf16x2<2>(w, nc), nibble_pair_to_bf16x2<3>(w, nc)};
                 }
             } else if constexpr (Q8) {
 #pragma unroll
@@ -917,7 +932,7 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
         for (int g = 0; g < 2; ++g)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool ok = !partial || (t.live[g] && tile * TILE + 16 * g + 4 * b + i < x.ntok);
+                const bool ok = 4 * b + i < lim[g];
                 float sc = scale_log2e;
                 vsc[g][i] = 1.f;
                 if constexpr (Q8) {
@@ -927,8 +942,7 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
                 xs[g][i] = ok ? (I4 ? s[g][i] - kcorr : s[g][i]) * sc : -INFINITY;
                 mx = fmaxf(mx, xs[g][i]);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = lane_blocks_max(mx);
         const float m_new = fmaxf(m, mx);
         if (__builtin_amdgcn_ballot_w64(m_new > m)) {   // rescale only when a running max grew
             const float alpha = fast_exp2(m - m_new);
@@ -982,13 +996,10 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
 
     // write the unit's result (final output, or its partial slot) and reset the softmax state
     auto finish = [&](const Unit &x) {
-        float lt = l + __shfl_xor(l, 16);
-        lt += __shfl_xor(lt, 32);
+        const float lt = lane_blocks_sum(l);
         float corr = 0.f;                       // 4-bit codes: 136 times the weights' sum (see prep_q)
         if constexpr (I4) {
-            float vt = vsum + __shfl_xor(vsum, 16);
-            vt += __shfl_xor(vt, 32);
-            corr = I4_BIAS * vt;
+            corr = I4_BIAS * lane_blocks_sum(vsum);
         }
         // accumulator of dim offset e (0..7) of the lane's 8-dim run i: MFMA j = e for bf16 and 8-bit
         // codes; for 4-bit codes MFMA j holds offset j / 2 + 4 (j % 2), so e comes from j = 2 e (e < 4) or

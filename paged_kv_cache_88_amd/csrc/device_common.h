@@ -106,6 +106,23 @@ __device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t w, int k) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max and sum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (one column of an MFMA result block), on the VALU:
+// with both operands the same register, v_permlane16_swap leaves lane l holding the values of lanes l & ~16
+// and l | 16, and v_permlane32_swap those of lanes l & ~32 and l | 32. Every lane of the four gets the same
+// value (max and + are commutative, and each step combines the same two values in every lane).
+__device__ __forceinline__ float lane_blocks_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float lane_blocks_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // D = A B + C on one 16x16x32 bf16 MFMA (fp32 accumulate). Lane l supplies A[l%16][8*(l/16) .. +8]

@@ -56,16 +56,6 @@ constexpr int SGB_MFMA = 0x008, SGB_DS_READ = 0x100;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// Max over lanes l, l^16, l^32 and l^48 (one column of an MFMA result block), on the VALU: with both
-// operands the same register, v_permlane16_swap leaves lane l holding the values of lanes l & ~16 and
-// l | 16, and v_permlane32_swap those of lanes l & ~32 and l | 32.
-__device__ __forceinline__ float max_lane_blocks(float x) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
 // ds_read_b64_tr_b16 at an LDS address (8 bytes, 8-byte aligned), as two dwords.
 __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *p) {
     const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)p);
@@ -349,7 +339,7 @@ prefill_kernel(uint16_t *__restrict__ out, const u32x4 *__restrict__ query, cons
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
                 mx = fmaxf(fmaxf(mx, fmaxf(s[kb][qb][0], s[kb][qb][1])), fmaxf(s[kb][qb][2], s[kb][qb][3]));
-            mx = max_lane_blocks(mx);
+            mx = lane_blocks_max(mx);
             m_new[qb] = fmaxf(m[qb], mx * scale_log2e);
             grow |= m_new[qb] > m[qb] + PF_RESCALE_SLACK;
         }
