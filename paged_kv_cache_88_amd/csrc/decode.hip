@@ -806,11 +806,13 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
             const int tokc = x.start + tlc;
             const int64_t blk = __builtin_amdgcn_readlane(xblk, (tokc >> log2_bs) - x.first_blk);
             t.live[g] = blk >= 0 && blk < num_blocks;
+            // a block outside the pool gets empty descriptors: its loads return zeros (finite K, V and scales)
             const int64_t slab = t.live[g] ? ((blk * num_kv_heads + x.kvh) << log2_bs) : 0;   // first row
+            const int range = t.live[g] ? (int)slab_bytes : 0;
             const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(key_cache + slab * RB), (short)0, (int)slab_bytes, BUF_RSRC_W3);
+                (void *)(key_cache + slab * RB), (short)0, range, BUF_RSRC_W3);
             const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(value_cache + slab * RB), (short)0, (int)slab_bytes, BUF_RSRC_W3);
+                (void *)(value_cache + slab * RB), (short)0, range, BUF_RSRC_W3);
             const int last = x.ntok - 1 - tl0;              // rows past it are clamped to it
             const int r0 = (tokc & bs_mask) - tlc + tl0;    // slab row of token tl0
             if constexpr (I4) {
@@ -828,9 +830,9 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
                 // scales of the 16-row group holding the clamped token (its own rows when the group is live)
                 const int srow = (tokc & bs_mask) & ~15;
                 const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
-                    (void *)(key_scale + slab), (short)0, 4 << log2_bs, BUF_RSRC_W3);
+                    (void *)(key_scale + slab), (short)0, t.live[g] ? 4 << log2_bs : 0, BUF_RSRC_W3);
                 const __amdgpu_buffer_rsrc_t vsr = __builtin_amdgcn_make_buffer_rsrc(
-                    (void *)(value_scale + slab), (short)0, 4 << log2_bs, BUF_RSRC_W3);
+                    (void *)(value_scale + slab), (short)0, t.live[g] ? 4 << log2_bs : 0, BUF_RSRC_W3);
                 t.ks[g] = __builtin_bit_cast(f32x4, buffer_load16(ksr, (srow + 4 * b) * 4));
                 t.vs[g] = __builtin_bit_cast(f32x4, buffer_load16(vsr, (srow + 4 * b) * 4));
             } else {
@@ -866,11 +868,8 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
     };
 
     auto compute = [&](const Unit &x, int tile, Tile &t) {
-        if constexpr (I4) {
-            if (tile == 0) prep_q();                // the unit's queries arrived with (or before) its first tile
-        }
-        // masked tokens: past the unit's end (only in its last tile), or in a block outside the pool,
-        // whose rows (block 0) may hold anything: those get V zeroed as well. Group g holds tile tokens
+        // masked tokens: past the unit's end (only in its last tile; their rows repeat the unit's last token),
+        // or in a block outside the pool (its loads returned zeros, see issue). Group g holds tile tokens
         // 16 g .. 16 g + 15, of which the first lim[g] (wave-uniform) are real; a lane's token 4 b + i of the
         // group is kept iff 4 b + i < lim[g] (one compare, no branch).
         int lim[2];
@@ -911,13 +910,6 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
 #pragma unroll
                 for (int i = 0; i < 4; ++i) tv[g][i] = t.v[g][i];
             }
-        }
-        if (!t.live[0] || !t.live[1]) {
-#pragma unroll
-            for (int g = 0; g < 2; ++g)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (!t.live[g]) tv[g][i] = u32x4{0, 0, 0, 0};
         }
         f32x4 s[2];
 #pragma unroll
@@ -1085,6 +1077,7 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
             ct = 0;
 #pragma unroll
             for (int c = 0; c < 4; ++c) qt[c] = qn[c];
+            if constexpr (I4) prep_q();         // here, not in compute: a per-tile test there became selects
             claimed = false;
             nxt_ready = false;
         }
@@ -1098,6 +1091,7 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
 
     Tile ta, tb;
     issue(cur, cur_blk, 0, ta);
+    if constexpr (I4) prep_q();
     while (step(ta, tb) && step(tb, ta)) {
     }
 }
