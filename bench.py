@@ -157,7 +157,8 @@ def measured_traffic(workload: str):
 def cpu_baseline(c, target_s=12.0, single_s=3.0):
     """Time the oracle (float64) on bounded samples of the same workload: on all host cores, the decode of
     the whole batch repeated until about target_s seconds of CPU work (fewer sequences if one pass is
-    already longer); and on one core, a sample of about single_s seconds."""
+    already longer); on one core, a sample of about single_s seconds; and its NumPy statement (BLAS
+    products, the BLAS thread count recorded) on a sample of about single_s seconds."""
     import oracle
 
     orc = oracle.default()
@@ -199,13 +200,38 @@ def cpu_baseline(c, target_s=12.0, single_s=3.0):
     nbytes1 = sample_bytes(sel1, reps1)
     orc.decode(c.dtype, c.query, kc, vc, c.block_tables, c.context_lens, c.scale, seqs=np.sort(order[:1]).astype(np.int32),
                nthreads=cores)                          # leave the oracle on all cores
+    # the NumPy statement of the same decode (oracle/numpy_decode.py: gathered blocks, BLAS products), timed on
+    # a sample of about single_s seconds, with the BLAS library's thread count
+    from oracle import numpy_decode
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [x for x in threadpool_info() if x.get("user_api") == "blas"]
+        blas_threads = int(sum(x.get("num_threads", 0) for x in blas)) or None
+        blas_lib = blas[0].get("internal_api") if blas else None
+    except ImportError:
+        blas_threads, blas_lib = None, None
+    probe = np.sort(order[:8]).astype(np.int32)
+    t0 = time.perf_counter()
+    numpy_decode.decode(c.dtype, c.query, kc, vc, c.block_tables, c.context_lens, c.scale, seqs=probe)
+    per_seq = (time.perf_counter() - t0) / len(probe)
+    kn = int(max(8, min(c.num_seqs, single_s / max(per_seq, 1e-9))))
+    seln = np.sort(order[:kn]).astype(np.int32)
+    t0 = time.perf_counter()
+    numpy_decode.decode(c.dtype, c.query, kc, vc, c.block_tables, c.context_lens, c.scale, seqs=seln)
+    dtn = time.perf_counter() - t0
+    nbytesn = sample_bytes(seln, 1)
+    numpy_leg = {"value": round(nbytesn / dtn / 1e9, 4), "unit": "GB/s", "blas_threads": blas_threads,
+                 "blas": blas_lib,
+                 "sample": f"decode of {kn} sequences ({int(c.context_lens[seln].sum())} context tokens), float64, "
+                           f"{dtn:.2f} s"}
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"decode of {len(sel)} of {c.num_seqs} sequences ({int(c.context_lens[sel].sum())} context tokens) "
                       f"x {reps} passes, float64, {dt:.2f} s",
             "seconds": round(dt, 3), "decode_tokens_per_s": round(reps * len(sel) / dt, 3),
             "single_core": {"value": round(nbytes1 / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
                             "sample": f"decode of {len(sel1)} sequences ({int(c.context_lens[sel1].sum())} context "
-                                      f"tokens) x {reps1} passes, float64, {dt1:.2f} s"}}
+                                      f"tokens) x {reps1} passes, float64, {dt1:.2f} s"},
+            "numpy": numpy_leg}
 
 
 def bench_ceilings(pkv, torch, dev, reps=10):
