@@ -742,7 +742,10 @@ decode_mfma_kernel(void *__restrict__ out, const void *__restrict__ query, const
     // until the list is done. (Waves do not run at equal rates: of two waves sharing a SIMD the older
     // one wins arbitration and streams up to twice as fast.) A wave stops at its first stratum whose
     // unit lies past the list.
-    const int C = gridDim.x, cu = blockIdx.x;
+    // (readfirstlane: without it the compiler treats the grid size and workgroup id as per-lane values, so
+    // every unit field derived from them sat in vector registers and each buffer descriptor built from one
+    // went through a waterfall loop)
+    const int C = __builtin_amdgcn_readfirstlane((int)gridDim.x), cu = __builtin_amdgcn_readfirstlane((int)blockIdx.x);
     auto unit_index = [&](int k) {
         const bool rev = ((k & 1) != 0) != (k > 0 && (k + 1) * C > nunits);
         return k * C + (rev ? C - 1 - cu : cu);
