@@ -15,7 +15,8 @@ over the timed steps), plus the roofline of the decode call measured with HIP ev
 stream (recorded around runs of ten back-to-back calls: each event costs the stream a few microseconds, so
 recording them around every call would slow the calls it measures), and the CPU oracle's rate
 on a bounded sample of the same workload. Secondary legs (not part of `value`): the same decode over
-int8, fp8 (E4M3) and int4 caches; the decode call on the other two decode workloads (batch 64 at block 256,
+int8, fp8 (E4M3) and int4 caches (whole calls, and runs from one shared plan as a model's layers would make
+them); the decode call on the other two decode workloads (batch 64 at block 256,
 batch 16 at 16k-32k tokens); the chunked-prefill workload on MFMA (bf16, int8 and fp8 caches); and the
 practical ceilings measured on the same GPU: the decode's read pattern (scrambled 4 KB and 64 KB chunks), the
 matrix cores' rate for the prefill's MFMA instruction, and a bf16 GEMM.
@@ -120,13 +121,33 @@ def bench_q8(kind, pkv, torch, W, c, dev, copies, steps, warmup):
         runs.append((e0, e1, min(steps, b + batch) - b))
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(z) / n for a, z, n in runs]))
+    finite = bool(torch.isfinite(out.float()).all().item())
+    # the same decode as a model's layers run it: one plan per step, then one run per layer from it
+    pkv.paged_attention_decode_plan(cl, c.max_context_len, c.num_heads, c.num_kv_heads, c.head_dim, c.block_size,
+                                    ws, dtype=torch.bfloat16, cache=kind, stream=stream)
+    run = getattr(pkv, decode_name + "_run")
+    runs = []
+    for b in range(0, steps, batch):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(b, min(steps, b + batch)):
+            kc, vc, ks, vs = pools[k % copies]
+            run(out, q, kc, vc, ks, vs, bt, c.max_context_len, c.scale, ws, stream=stream)
+        e1.record(stream)
+        runs.append((e0, e1, min(steps, b + batch) - b))
+    torch.cuda.synchronize()
+    run_ms = float(np.mean([a.elapsed_time(z) / n for a, z, n in runs]))
     nbytes = decode_bytes_q4(c) if kind == "int4" else decode_bytes_q8(c)
     return {"workload": c.name, "cache": what,
             "decode_ms": round(ms, 5), "algorithmic_bytes": nbytes,
             "achieved_gbs": round(nbytes / (ms * 1e-3) / 1e9, 2),
             "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "decode_tokens_per_s": round(c.num_seqs / (ms * 1e-3), 1),
-            "outputs_finite": bool(torch.isfinite(out.float()).all().item())}
+            "per_layer_run": {"run_ms": round(run_ms, 5),
+                              "frac_of_hbm_peak": round(nbytes / (run_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "what": "one paged_attention_decode_plan per step, then the "
+                                      f"{decode_name}_run of each layer from it (the plan's kernel is outside)"},
+            "outputs_finite": finite and bool(torch.isfinite(out.float()).all().item())}
 
 
 def store_bytes(c) -> int:
